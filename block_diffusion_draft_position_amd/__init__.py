@@ -1,0 +1,12 @@
+"""MI355X-native DDTree verification round.
+
+The work happens in libddt.so (include/ddt.h): hand-written HIP kernels for gfx950.
+This package is its thin Python binding (PyTorch supplies device memory and streams)
+and its build script.
+"""
+from ._lib import (  # noqa: F401
+    DDT_BF16, DDT_F32, DDTError, EXPORTS, LIB_PATH, attention_profiling, attention_timing,
+    attention_workspace_size, ddt_build_tree,
+    ddt_topk, ddt_tree_attention, ddt_tree_mask, ddt_tree_walk, load,
+)
+from .round import Shape, VerifyRound  # noqa: F401

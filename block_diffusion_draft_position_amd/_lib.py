@@ -1,0 +1,236 @@
+"""ctypes binding of libddt.so (include/ddt.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.  PyTorch
+supplies device memory and the current stream.  If the library is missing the
+import of this module succeeds but every call raises, naming the build command.
+"""
+import ctypes
+import math
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libddt.so")
+
+DDT_F32, DDT_BF16 = 0, 1
+MAX_K, MAX_L, MAX_B = 64, 64, 1023
+
+_lib = None
+
+
+class DDTError(RuntimeError):
+    pass
+
+
+def _p(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def load() -> ctypes.CDLL:
+    """Load libddt.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise DDTError(f"{LIB_PATH} is missing: build it with "
+                       "`python -m block_diffusion_draft_position_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "ddt_status_string": (ctypes.c_char_p, [i32]),
+        "ddt_topk_workspace_size": (sz, [i64, i64, i32]),
+        "ddt_topk": (i32, [vp, i64, i64, i64, i32, vp, vp, vp, sz, vp]),
+        "ddt_build_tree": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "ddt_tree_mask": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp]),
+        "ddt_tree_attention_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i64]),
+        "ddt_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     f32, i64, vp, vp, vp, sz, vp]),
+        "ddt_tree_walk_workspace_size": (sz, [i32, i32, i64]),
+        "ddt_tree_walk": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]),
+        "ddt_attention_profiling": (i32, [i32]),
+        "ddt_attention_timing": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_build_tree",
+           "ddt_tree_mask", "ddt_tree_attention_workspace_size", "ddt_tree_attention",
+           "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_attention_profiling",
+           "ddt_attention_timing")
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().ddt_status_string(status).decode()
+        raise DDTError(f"{what}: {msg} (status {status})")
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- entry points
+def ddt_topk(logits: torch.Tensor, k: int, out_tok=None, out_logq=None, ws=None):
+    """logits [..., V] fp32 -> (tok [..., k] int32, logq [..., k] fp32)."""
+    lib = load()
+    _dev(logits, "logits", torch.float32)
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    lead = tuple(logits.shape[:-1])
+    if out_tok is None:
+        out_tok = torch.empty(lead + (k,), dtype=torch.int32, device=logits.device)
+    if out_logq is None:
+        out_logq = torch.empty(lead + (k,), dtype=torch.float32, device=logits.device)
+    need = lib.ddt_topk_workspace_size(rows, V, k)
+    if ws is None:
+        ws = _ws(need, logits.device)
+    _check(lib.ddt_topk(_p(logits), rows, V, V, k, _p(out_tok), _p(out_logq), _p(ws), ws.numel(),
+                        _stream(logits.device)), "ddt_topk")
+    return out_tok, out_logq
+
+
+def ddt_build_tree(topk_tok: torch.Tensor, topk_logq: torch.Tensor, bonus: torch.Tensor, B: int,
+                   out: Optional[Dict[str, torch.Tensor]] = None, with_logq: bool = True):
+    """[S,L,K] top-K tokens/logq + bonus [S] -> canonical tree dict ([S,B+1] arrays)."""
+    lib = load()
+    S, L, K = topk_tok.shape
+    _dev(topk_tok, "topk_tok", torch.int32)
+    _dev(topk_logq, "topk_logq", torch.float32, (S, L, K))
+    _dev(bonus, "bonus", torch.int32, (S,))
+    dev = topk_tok.device
+    N = B + 1
+    if out is None:
+        out = {"tree_tok": torch.empty(S, N, dtype=torch.int32, device=dev),
+               "parent": torch.empty(S, N, dtype=torch.int32, device=dev),
+               "depth": torch.empty(S, N, dtype=torch.int32, device=dev),
+               "node_logq": torch.empty(S, N, dtype=torch.float32, device=dev) if with_logq else None,
+               "num_nodes": torch.empty(S, dtype=torch.int32, device=dev)}
+    _check(lib.ddt_build_tree(_p(topk_tok), _p(topk_logq), _p(bonus), S, L, K, B,
+                              _p(out["tree_tok"]), _p(out["parent"]), _p(out["depth"]),
+                              _p(out.get("node_logq")), _p(out["num_nodes"]), _stream(dev)),
+           "ddt_build_tree")
+    return out
+
+
+def ddt_tree_mask(parent: torch.Tensor, depth: torch.Tensor, num_nodes: torch.Tensor,
+                  cu_prefix: Optional[torch.Tensor], mask=None, pos_ids=None):
+    """-> (mask [S,N,W] int32 view of uint32 bits, pos_ids [S,N] or None)."""
+    lib = load()
+    S, N = parent.shape
+    _dev(parent, "parent", torch.int32)
+    _dev(depth, "depth", torch.int32, (S, N))
+    _dev(num_nodes, "num_nodes", torch.int32, (S,))
+    if cu_prefix is not None:
+        _dev(cu_prefix, "cu_prefix", torch.int64, (S + 1,))
+    W = (N + 31) // 32
+    dev = parent.device
+    if mask is None:
+        mask = torch.empty(S, N, W, dtype=torch.int32, device=dev)
+    if pos_ids is None and cu_prefix is not None:
+        pos_ids = torch.empty(S, N, dtype=torch.int32, device=dev)
+    _check(lib.ddt_tree_mask(_p(parent), _p(depth), _p(num_nodes), _p(cu_prefix), S, N - 1,
+                             _p(mask), _p(pos_ids), _stream(dev)), "ddt_tree_mask")
+    return mask, pos_ids
+
+
+def attention_workspace_size(S, B, Hq, Hkv, D, dtype, max_prefix) -> int:
+    return int(load().ddt_tree_attention_workspace_size(S, B, Hq, Hkv, D, dtype, max_prefix))
+
+
+def ddt_tree_attention(q, k_cache, v_cache, cu_prefix, k_tree, v_tree, mask, num_nodes,
+                       scale: Optional[float] = None, max_prefix: Optional[int] = None,
+                       with_lse: bool = True, out=None, lse=None, ws=None):
+    """q [S,N,Hq,D]; k/v_cache [T,Hkv,D]; k/v_tree [S,N,Hkv,D] (fp32 or bf16) ->
+    (out [S,N,Hq,D], lse [S,N,Hq] fp32 or None)."""
+    lib = load()
+    S, N, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    dt = {torch.float32: DDT_F32, torch.bfloat16: DDT_BF16}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_tree", k_tree),
+                    ("v_tree", v_tree)):
+        _dev(t, name, q.dtype)
+    if k_cache.shape != v_cache.shape or k_cache.shape[2] != D:
+        raise ValueError("k_cache/v_cache must be [T, Hkv, D]")
+    _dev(k_tree, "k_tree", q.dtype, (S, N, Hkv, D))
+    _dev(v_tree, "v_tree", q.dtype, (S, N, Hkv, D))
+    _dev(cu_prefix, "cu_prefix", torch.int64, (S + 1,))
+    _dev(mask, "mask", None, (S, N, (N + 31) // 32))
+    _dev(num_nodes, "num_nodes", torch.int32, (S,))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_prefix is None:
+        cu = cu_prefix.cpu()
+        max_prefix = int((cu[1:] - cu[:-1]).max())
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty(S, N, Hq, dtype=torch.float32, device=dev)
+    need = lib.ddt_tree_attention_workspace_size(S, N - 1, Hq, Hkv, D, dt, max_prefix)
+    if ws is None:
+        ws = _ws(need, dev)
+    _check(lib.ddt_tree_attention(_p(q), _p(k_cache), _p(v_cache), _p(cu_prefix), _p(k_tree),
+                                  _p(v_tree), _p(mask), _p(num_nodes), S, N - 1, Hq, Hkv, D, dt,
+                                  float(scale), int(max_prefix), _p(out), _p(lse if with_lse else None),
+                                  _p(ws), ws.numel(), _stream(dev)), "ddt_tree_attention")
+    return out, (lse if with_lse else None)
+
+
+def ddt_tree_walk(tree_tok, parent, num_nodes, target_logits, L: int, out=None, ws=None):
+    """target_logits [S,N,V] fp32 -> dict(accept_len [S], acc_nodes [S,L], acc_tok [S,L], bonus [S])."""
+    lib = load()
+    S, N = tree_tok.shape
+    _dev(tree_tok, "tree_tok", torch.int32)
+    _dev(parent, "parent", torch.int32, (S, N))
+    _dev(num_nodes, "num_nodes", torch.int32, (S,))
+    _dev(target_logits, "target_logits", torch.float32)
+    if target_logits.shape[:2] != (S, N):
+        raise ValueError("target_logits must be [S, N, V]")
+    V = target_logits.shape[2]
+    dev = tree_tok.device
+    if out is None:
+        out = {"accept_len": torch.empty(S, dtype=torch.int32, device=dev),
+               "acc_nodes": torch.empty(S, L, dtype=torch.int32, device=dev),
+               "acc_tok": torch.empty(S, L, dtype=torch.int32, device=dev),
+               "bonus": torch.empty(S, dtype=torch.int32, device=dev)}
+    need = lib.ddt_tree_walk_workspace_size(S, N - 1, V)
+    if ws is None:
+        ws = _ws(need, dev)
+    _check(lib.ddt_tree_walk(_p(tree_tok), _p(parent), _p(num_nodes), _p(target_logits), S, N - 1,
+                             L, V, _p(out["accept_len"]), _p(out["acc_nodes"]), _p(out["acc_tok"]),
+                             _p(out["bonus"]), _p(ws), ws.numel(), _stream(dev)), "ddt_tree_walk")
+    return out
+
+
+def attention_profiling(enable: bool):
+    _check(load().ddt_attention_profiling(1 if enable else 0), "ddt_attention_profiling")
+
+
+def attention_timing() -> Tuple[float, int]:
+    """(summed milliseconds, launches) of the attention main kernel since the last read."""
+    t, n = ctypes.c_double(0.0), ctypes.c_int(0)
+    _check(load().ddt_attention_timing(ctypes.byref(t), ctypes.byref(n)), "ddt_attention_timing")
+    return t.value, n.value

@@ -283,7 +283,9 @@ def candidate_logprobs(logq: np.ndarray) -> np.ndarray:
 
 def selection_gap(logq: np.ndarray, B: int) -> float:
     """log-prob of the B-th selected prefix minus that of the best unselected one
-    (+inf when the candidate tree holds at most B prefixes)."""
+    (+inf when B = 0 or the candidate tree holds at most B prefixes)."""
+    if B <= 0:
+        return float("inf")
     taken = best_first_prefixes(logq, B + 1)
     if len(taken) <= B:
         return float("inf")

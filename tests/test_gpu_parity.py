@@ -1,0 +1,200 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integers (top-K tokens, tree, mask, positions, walk) must match exactly; floats
+within the tolerances of tests/_gpu.py.  Small shapes span several key tiles,
+several splits and ragged tails; the full workloads compare every integer output
+and a sample of attention rows that the oracle computes one by one.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_draft_position_amd as ddt
+import oracle
+from ddt_synthetic import configs, gen
+
+from _cases import attempts
+from _gpu import (NODE_LOGQ_ATOL, TOPK_ATOL, check_attention_rows, dev_tensor, target_for, upload,
+                  widen)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ddt.load()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_case(cfg, att=None, rows_per_seq=None, sharp=False, seed_rows=0):
+    """Full round on the GPU and in the oracle; compare everything."""
+    _say(f"[case] {cfg.name} S={cfg.S} L={cfg.L} V={cfg.V} K={cfg.K} B={cfg.B} P={cfg.prefix} "
+         f"Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} {cfg.dtype} sharp={sharp}")
+    if att is None:
+        att = attempts(cfg)
+    b = gen.batch(cfg, att)
+    if sharp:
+        _sharpen(cfg, b)
+    scale = 1.0 / math.sqrt(cfg.D)
+    # ---- oracle: steps 1-3 for every sequence
+    trees, tk = {}, {}
+    for s in range(cfg.S):
+        tok, lq = oracle.topk(b["draft_logits"][s], cfg.K)
+        tk[s] = (tok, lq)
+        trees[s] = oracle.build_tree(tok, lq, int(b["bonus"][s]), cfg.B)
+    tl = target_for(cfg, b, trees)
+    # ---- GPU
+    d = upload(b)
+    d["target"] = dev_tensor(tl)
+    tok, lq = ddt.ddt_topk(d["draft_logits"], cfg.K)
+    tree = ddt.ddt_build_tree(tok, lq, d["bonus"], cfg.B)
+    mask, pos = ddt.ddt_tree_mask(tree["parent"], tree["depth"], tree["num_nodes"], d["cu_prefix"])
+    out, lse = ddt.ddt_tree_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_prefix"], d["k_tree"],
+                                      d["v_tree"], mask, tree["num_nodes"], scale)
+    walk = ddt.ddt_tree_walk(tree["tree_tok"], tree["parent"], tree["num_nodes"], d["target"], cfg.L)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in tree.items() if v is not None}
+    gw = {k: v.cpu().numpy() for k, v in walk.items()}
+    gtok, glq = tok.cpu().numpy(), lq.cpu().numpy()
+    gmask = mask.cpu().numpy().view(np.uint32)
+    gpos = pos.cpu().numpy()
+    rng = np.random.default_rng(1000 + seed_rows)
+    for s in range(cfg.S):
+        t = trees[s]
+        nn = int(t["num_nodes"])
+        assert np.array_equal(gtok[s], tk[s][0]), f"seq {s}: top-K tokens"
+        np.testing.assert_allclose(glq[s], tk[s][1], rtol=0, atol=TOPK_ATOL, err_msg=f"seq {s}: logq")
+        assert int(g["num_nodes"][s]) == nn, f"seq {s}: num_nodes"
+        for k in ("tree_tok", "parent", "depth"):
+            assert np.array_equal(g[k][s], t[k]), f"seq {s}: {k}"
+        np.testing.assert_allclose(g["node_logq"][s][:nn], t["node_logq"][:nn], rtol=0,
+                                   atol=NODE_LOGQ_ATOL)
+        assert np.all(np.isneginf(g["node_logq"][s][nn:]))
+        P = int(b["prefix_lens"][s])
+        m_ref = oracle.tree_mask(t["parent"], nn, cfg.N)
+        assert np.array_equal(gmask[s], m_ref), f"seq {s}: mask"
+        assert np.array_equal(gpos[s], oracle.position_ids(t["depth"], nn, P)), f"seq {s}: pos"
+        w = oracle.tree_walk(t["tree_tok"], t["parent"], nn, tl[s], cfg.L)
+        assert int(gw["accept_len"][s]) == int(w["accept_len"]), f"seq {s}: accept_len"
+        assert np.array_equal(gw["acc_nodes"][s], w["acc_nodes"]) and np.array_equal(gw["acc_tok"][s], w["acc_tok"])
+        assert int(gw["bonus"][s]) == int(w["bonus"]), f"seq {s}: bonus"
+        # attention: all rows, or a sample
+        all_rows = [(n, h) for n in range(cfg.N) for h in range(cfg.Hq)]
+        if rows_per_seq is None or rows_per_seq >= len(all_rows):
+            rows = all_rows
+        else:
+            deep = int(np.argmax(t["depth"][:nn]))
+            pick = set(map(tuple, [all_rows[i] for i in rng.choice(len(all_rows), rows_per_seq, replace=False)]))
+            pick |= {(deep, h) for h in range(min(cfg.Hq, 4))} | {(0, 0), (nn - 1, cfg.Hq - 1)}
+            if nn < cfg.N:
+                pick |= {(cfg.N - 1, 0)}
+            rows = sorted(pick)
+        p0, p1 = int(b["cu_prefix"][s]), int(b["cu_prefix"][s + 1])
+        ref_o, ref_l = oracle.tree_attention(oracle.round.widen(b["q"][s]), oracle.round.widen(b["k_cache"][p0:p1]),
+                                             oracle.round.widen(b["v_cache"][p0:p1]), oracle.round.widen(b["k_tree"][s]),
+                                             oracle.round.widen(b["v_tree"][s]), m_ref, nn, scale, rows)
+        go = widen(out[s])
+        gl = lse[s].cpu().numpy().astype(np.float64)
+        idx_n = np.array([r[0] for r in rows])
+        idx_h = np.array([r[1] for r in rows])
+        check_attention_rows(go[idx_n, idx_h], ref_o, cfg.dtype, f"{cfg.name} seq {s}")
+        valid = idx_n < nn
+        np.testing.assert_allclose(gl[idx_n[valid], idx_h[valid]], ref_l[valid], rtol=0,
+                                   atol=1e-5 if cfg.dtype == "f32" else 1e-3)
+        assert np.all(np.isneginf(gl[idx_n[~valid], idx_h[~valid]]))
+    return gw
+
+
+def _sharpen(cfg, b):
+    """Make the tree keys dominate the softmax so that a mask error cannot hide under a
+    long prefix: every query and tree key leans on one direction u per (seq, KV head)."""
+    rng = np.random.default_rng(77)
+    a = math.sqrt(10.0 * math.sqrt(cfg.D))
+    enc = (lambda x: gen.f32_to_bf16_bits(x)) if cfg.dtype == "bf16" else (lambda x: x.astype(np.float32))
+    dec = (lambda x: gen.bf16_bits_to_f32(x)) if cfg.dtype == "bf16" else (lambda x: x)
+    G = cfg.Hq // cfg.Hkv
+    q = dec(b["q"]).copy()
+    kt = dec(b["k_tree"]).copy()
+    for s in range(cfg.S):
+        for g in range(cfg.Hkv):
+            u = rng.standard_normal(cfg.D)
+            u /= np.linalg.norm(u)
+            q[s, :, g * G:(g + 1) * G, :] += (a * u).astype(np.float32)
+            kt[s, :, g, :] = (a * u).astype(np.float32) + 0.3 * rng.standard_normal((cfg.N, cfg.D))
+    b["q"] = enc(q)
+    b["k_tree"] = enc(kt)
+
+
+# ----------------------------------------------------------------------------- small shapes
+MID = dict(S=3, L=5, V=3000, K=4, B=40, prefix=(0, 700), Hq=8, Hkv=2)
+
+
+@pytest.mark.parametrize("D", [128, 64, 32])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mid_shapes(D, dtype):
+    cfg = configs.custom(f"mid-{dtype}-D{D}", D=D, dtype=dtype, **MID)
+    run_case(cfg)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sharp_tree_keys(dtype):
+    cfg = configs.custom(f"sharp-{dtype}", S=2, L=6, V=500, K=3, B=50, prefix=(2000, 2600),
+                         Hq=8, Hkv=2, D=128, dtype=dtype)
+    run_case(cfg, sharp=True)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("B0", dict(B=0)), ("B1", dict(B=1)), ("K1", dict(K=1, B=7)), ("L1", dict(L=1, K=6, B=6)),
+    ("P0", dict(prefix=(0, 0))), ("P1", dict(prefix=(1, 1))), ("P7", dict(prefix=(7, 7))),
+    ("shortfall", dict(L=2, K=3, B=20)), ("wide", dict(K=64, B=200, L=3, V=400)),
+    ("deep", dict(L=64, K=2, B=150, V=40)), ("gqa8", dict(Hq=16, Hkv=2)), ("mha", dict(Hq=4, Hkv=4)),
+])
+def test_edge_cases(name, kw):
+    base = dict(S=2, L=4, V=257, K=4, B=12, prefix=(5, 150), Hq=8, Hkv=2, D=128, dtype="bf16")
+    base.update(kw)
+    cfg = configs.custom(f"edge-{name}", **base)
+    run_case(cfg)
+
+
+def test_large_budget_multi_word_mask():
+    cfg = configs.custom("bigB", S=1, L=8, V=1000, K=16, B=700, prefix=(300, 300), Hq=4, Hkv=1,
+                         D=64, dtype="bf16")
+    run_case(cfg)
+
+
+def test_tiny_workload_many_draws():
+    cfg = dataclasses.replace(configs.C0, S=16)   # sequences 0..15 of the tiny workload
+    w = run_case(cfg)
+    _say("tiny accept lengths", w["accept_len"].tolist())
+
+
+def test_deterministic():
+    cfg = configs.custom("det", S=2, L=6, V=5000, K=8, B=60, prefix=(900, 1300), Hq=8, Hkv=2,
+                         D=128, dtype="bf16")
+    b = gen.batch(cfg)
+    d = upload(b)
+    outs = []
+    for _ in range(2):
+        tok, lq = ddt.ddt_topk(d["draft_logits"], cfg.K)
+        tree = ddt.ddt_build_tree(tok, lq, d["bonus"], cfg.B)
+        mask, _ = ddt.ddt_tree_mask(tree["parent"], tree["depth"], tree["num_nodes"], None)
+        out, lse = ddt.ddt_tree_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_prefix"],
+                                          d["k_tree"], d["v_tree"], mask, tree["num_nodes"])
+        outs.append([x.cpu() for x in (tok, lq, tree["tree_tok"], mask, out.view(torch.int16), lse)])
+    for a, b2 in zip(*outs):
+        assert torch.equal(a, b2)
+
+
+# ----------------------------------------------------------------------------- full workloads
+@pytest.mark.parametrize("name,rows", [("C0", None), ("C1", 200), ("C2", 48), ("C3-B16", 64),
+                                       ("C3-B128", 64), ("C3-B512", 64), ("C4", 12)])
+def test_full_workloads(name, rows):
+    run_case(configs.get(name), rows_per_seq=rows)
