@@ -56,9 +56,11 @@ hipEvent_t prof_begin(hipStream_t st) {
     p.pool.emplace_back(a, b);
   }
   auto& ev = p.pool[p.used++];
-  if (hipEventRecord(ev.first, st) != hipSuccess) return nullptr;
+  if (prof_record(ev.first, st) != hipSuccess) return nullptr;
   return ev.second;
 }
+
+hipError_t prof_record(hipEvent_t ev, hipStream_t st) { return hipEventRecord(ev, st); }
 
 }  // namespace ddt
 

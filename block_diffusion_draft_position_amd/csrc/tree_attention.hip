@@ -561,7 +561,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   }
   if (e != hipSuccess) return e;
   if (stop) {
-    e = hipEventRecord(stop, st);
+    e = prof_record(stop, st);
     if (e != hipSuccess) return e;
   }
   const int64_t total = (int64_t)S * N * Hq;

@@ -200,12 +200,12 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
 /* ---------------------------------------------------------------- benchmark aid
  * Timing of the attention's main kernel (the round's dominant kernel) with HIP
  * events on the stream it runs on.  While profiling is on, every
- * ddt_tree_attention call records a start/stop event pair around that kernel
- * (inside a HIP graph capture the pair becomes part of the graph and is
- * re-recorded by every replay).  ddt_attention_timing waits for the recorded
- * pairs, returns the sum of their elapsed times in milliseconds and their count,
- * and forgets them.  ddt_attention_profiling(0) releases the events.  This is the
- * only state the library keeps; it is process-wide and guarded by a mutex.
+ * ddt_tree_attention call records a start/stop event pair around that kernel.
+ * Use it on eagerly launched calls: event pairs recorded during a HIP graph
+ * capture are not readable afterwards.  ddt_attention_timing waits for the
+ * recorded pairs, returns the sum of their elapsed times in milliseconds and their
+ * count, and forgets them.  ddt_attention_profiling(0) releases the events.  This
+ * is the only state the library keeps; it is process-wide and guarded by a mutex.
  * Returns DDT_OK or DDT_ERR_HIP.
  */
 int ddt_attention_profiling(int enable);
