@@ -12,7 +12,9 @@
 // entries, and the frontier never holds more than one entry per selected node.
 //
 // Entries live in registers: node u at lane u % 64, slot u / 64.  Each lane caches
-// its best slot; a pop is one wave max-reduction plus two exec-masked updates.
+// its best slot; a pop is one DPP max-reduction plus two exec-masked updates.  The
+// top-K log-probabilities sit in registers too (depth row = register, rank = lane),
+// so a pop reads them with v_readlane instead of an LDS round trip.
 // Scores are summed in fp64; the comparison key is the fp32 rounding of that sum
 // (rounding is monotone, so a child's key never exceeds its parent's and the popped
 // set stays prefix-closed).
@@ -50,7 +52,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-template <int J>
+template <int J, int LM>
 __global__ void __launch_bounds__(kWave)
 build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict__ topk_logq,
                   const int32_t* __restrict__ bonus, int L, int K, int B,
@@ -83,33 +85,31 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
   }
   const float* lq_g = topk_logq + (int64_t)s * LK;
   const int32_t* tok_g = topk_tok + (int64_t)s * LK;
-  for (int i = lane; i < LK; i += kWave) {
-    sm.lq[i] = lq_g[i];
-    sm.ltok[i] = tok_g[i];
-  }
+  // logq table in registers: ltab[d] holds depth-row d, rank = lane (K <= 64)
+  float ltab[LM];
+#pragma unroll
+  for (int d = 0; d < LM; ++d) ltab[d] = (d < L && lane < K) ? lq_g[d * K + lane] : -INFINITY;
+  for (int i = lane; i < LK; i += kWave) sm.ltok[i] = tok_g[i];
   for (int i = lane; i < N; i += kWave) sm.nkids[i] = 0;
-  __syncthreads();
-
-  // lane d holds the rank-0 logq of depth row d (d < L <= 64)
-  const float l0v = lane < L ? sm.lq[lane * K] : -INFINITY;
 
   // frontier entries, node u at (lane u % 64, slot u / 64)
   float key[J];
   double ex[J];     // exact key: score(u) + logq[depth(u)][cursor(u)]
   double sc[J];     // score(u)
-  int dep[J];       // depth(u)
-  int cur[J];       // cursor(u): rank of u's next child = children selected so far
+  int meta[J];      // depth(u) | cursor(u) << 8; cursor = rank of u's next child
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     key[j] = -INFINITY;
     ex[j] = 0.0;
     sc[j] = 0.0;
-    dep[j] = 0;
-    cur[j] = 0;
+    meta[j] = 0;
   }
-  if (lane == 0) {  // the root
-    ex[0] = (double)readlane(l0v, 0);
-    key[0] = (float)ex[0];
+  {
+    const float r0 = readlane(ltab[0], 0);
+    if (lane == 0) {  // the root's first child
+      ex[0] = (double)r0;
+      key[0] = r0;
+    }
   }
   float bkey = key[0];
   int bslot = 0;
@@ -119,50 +119,45 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
     const float M = wave_max(bkey);
     if (M == -INFINITY) break;  // candidate tree exhausted
     const int w = __ffsll((long long)ballot(bkey == M)) - 1;
-    const int j = __builtin_amdgcn_readfirstlane(readlane(bslot, w));
-    const int u = j * kWave + w;
+    const int j = J == 1 ? 0 : __builtin_amdgcn_readfirstlane(readlane(bslot, w));
     const double ex_u = readlane_f64(ex[j], w);
     const double sc_u = readlane_f64(sc[j], w);
-    const int dep_u = readlane(dep[j], w);
-    const int cur_u = readlane(cur[j], w);
-    const int c = n++;  // the selected child
+    const int meta_u = __builtin_amdgcn_readfirstlane(readlane(meta[j], w));
+    const int dep_u = meta_u & 0xff;
+    const int nc = (meta_u >> 8) + 1;  // u's next child rank
+    const int c = n++;                 // the selected child
     const int dep_c = dep_u + 1;
+    const float l_sib = nc < K ? readlane(ltab[dep_u], nc) : -INFINITY;
+    const float l_kid = dep_c < L ? readlane(ltab[dep_c < LM ? dep_c : 0], 0) : -INFINITY;
     if (lane == 0) {
-      sm.parent[c] = u;
-      sm.rank[c] = cur_u;
+      sm.parent[c] = j * kWave + w;
+      sm.rank[c] = nc - 1;
       sm.depth[c] = dep_c;
       sm.score[c] = ex_u;
     }
     // u moves on to its next child
     if (lane == w) {
-      const int nc = cur_u + 1;
-      cur[j] = nc;
-      if (nc < K) {
-        const double e = sc_u + (double)sm.lq[dep_u * K + nc];
-        ex[j] = e;
-        key[j] = (float)e;
-      } else {
-        key[j] = -INFINITY;
-      }
-      bkey = -INFINITY;
+      const double e = sc_u + (double)l_sib;
+      meta[j] = dep_u | (nc << 8);
+      ex[j] = e;
+      key[j] = l_sib == -INFINITY ? -INFINITY : (float)e;
+      bkey = key[0];
+      bslot = 0;
 #pragma unroll
-      for (int i = 0; i < J; ++i)
+      for (int i = 1; i < J; ++i)
         if (key[i] > bkey) {
           bkey = key[i];
           bslot = i;
         }
     }
     // c starts at its first child
-    const int lc = c % kWave;
     const int jc = c / kWave;
-    if (lane == lc && jc < J) {
-      const bool open = dep_c < L;
-      const double e = open ? ex_u + (double)readlane(l0v, dep_c) : 0.0;
-      const float kk = open ? (float)e : -INFINITY;
+    if (lane == c % kWave && jc < J) {
+      const double e = ex_u + (double)l_kid;
+      const float kk = l_kid == -INFINITY ? -INFINITY : (float)e;
       ex[jc] = e;
       sc[jc] = ex_u;
-      dep[jc] = dep_c;
-      cur[jc] = 0;
+      meta[jc] = dep_c;
       key[jc] = kk;
       if (kk > bkey) {
         bkey = kk;
@@ -174,7 +169,7 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int u = j * kWave + lane;
-    if (u < n) sm.nkids[u] = cur[j];
+    if (u < n) sm.nkids[u] = meta[j] >> 8;
   }
   if (lane == 0) {
     sm.parent[0] = -1;
@@ -233,7 +228,7 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
   if (lane == 0) num_nodes[s] = n;
 }
 
-template <int J>
+template <int J, int LM>
 hipError_t launch_j(const int32_t* tok, const float* logq, const int32_t* bonus, int S, int L,
                     int K, int B, int32_t* tree_tok, int32_t* parent, int32_t* depth,
                     float* node_logq, int32_t* num_nodes, hipStream_t st) {
@@ -241,13 +236,22 @@ hipError_t launch_j(const int32_t* tok, const float* logq, const int32_t* bonus,
   const size_t smem = sizeof(double) * N + (sizeof(float) + sizeof(int)) * (size_t)L * K +
                       sizeof(int) * 7 * (size_t)N;
   if (smem > 48 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_tree_kernel<J>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_tree_kernel<J, LM>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(build_tree_kernel<J>, dim3(S), dim3(kWave), smem, st, tok, logq, bonus, L, K,
-                     B, tree_tok, parent, depth, node_logq, num_nodes);
+  hipLaunchKernelGGL((build_tree_kernel<J, LM>), dim3(S), dim3(kWave), smem, st, tok, logq, bonus,
+                     L, K, B, tree_tok, parent, depth, node_logq, num_nodes);
   return hipGetLastError();
+}
+
+template <int J>
+hipError_t launch_l(const int32_t* tok, const float* logq, const int32_t* bonus, int S, int L,
+                    int K, int B, int32_t* tree_tok, int32_t* parent, int32_t* depth,
+                    float* node_logq, int32_t* num_nodes, hipStream_t st) {
+  if (L <= 16)
+    return launch_j<J, 16>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq, num_nodes, st);
+  return launch_j<J, 64>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq, num_nodes, st);
 }
 
 }  // namespace
@@ -260,7 +264,7 @@ hipError_t launch_build_tree(const int32_t* tok, const float* logq, const int32_
   // are ever created (the last selected node's entry is never popped).
   const int slots = (int)ceil_div(B + 1, kWave);
 #define DDT_J(JJ) \
-  return launch_j<JJ>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq, num_nodes, st)
+  return launch_l<JJ>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq, num_nodes, st)
   if (slots <= 1) DDT_J(1);
   if (slots <= 2) DDT_J(2);
   if (slots <= 4) DDT_J(4);

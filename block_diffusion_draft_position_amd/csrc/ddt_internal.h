@@ -34,16 +34,111 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
 }
 
+// ---- cross-lane exchange without LDS: DPP row permutes and the gfx950 permlane swaps.
+// xchg<S>(v) returns the value of a partner lane in the other half of v's aligned
+// group of 2S lanes (S = 1, 2, 4, 8, 16, 32).  For S = 4 and 8 the partner is the
+// mirrored lane, not lane ^ S; any pairing of the two halves serves a butterfly
+// reduction.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v, int old) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, 0xf, 0xf, false);
+}
+
+template <int S>
+__device__ __forceinline__ int xchg(int v) {
+  if constexpr (S == 1) return dpp<0xB1>(v, v);   // quad_perm [1,0,3,2]
+  if constexpr (S == 2) return dpp<0x4E>(v, v);   // quad_perm [2,3,0,1]
+  if constexpr (S == 4) return dpp<0x141>(v, v);  // row_half_mirror
+  if constexpr (S == 8) return dpp<0x140>(v, v);  // row_mirror
+  // The swaps exchange 16-lane rows (S = 16) or 32-lane halves (S = 32) between
+  // two registers; with v in both, one result is v and the other is the partner.
+  if constexpr (S == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)(p[0] == (unsigned)v ? p[1] : p[0]);
+  }
+  if constexpr (S == 32) {
+    const auto p = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)(p[0] == (unsigned)v ? p[1] : p[0]);
+  }
+}
+
+template <int S>
+__device__ __forceinline__ float xchg(float v) {
+  return __builtin_bit_cast(float, xchg<S>(__builtin_bit_cast(int, v)));
+}
+
+template <int S>
+__device__ __forceinline__ double xchg(double v) {
+  const long long b = __builtin_bit_cast(long long, v);
+  const int lo = xchg<S>((int)(b & 0xffffffff));
+  const int hi = xchg<S>((int)(b >> 32));
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Reductions over the wave; every lane receives the result.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = fmaxf(v, xchg<1>(v));
+  v = fmaxf(v, xchg<2>(v));
+  v = fmaxf(v, xchg<4>(v));
+  v = fmaxf(v, xchg<8>(v));
+  v = fmaxf(v, xchg<16>(v));
+  v = fmaxf(v, xchg<32>(v));
   return v;
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  v += xchg<1>(v);
+  v += xchg<2>(v);
+  v += xchg<4>(v);
+  v += xchg<8>(v);
+  v += xchg<16>(v);
+  v += xchg<32>(v);
   return v;
+}
+
+// (value, id) pairs under `better`
+template <int S>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = xchg<S>(v);
+  const int oi = xchg<S>(i);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<1>(v, i);
+  argmax_step<2>(v, i);
+  argmax_step<4>(v, i);
+  argmax_step<8>(v, i);
+  argmax_step<16>(v, i);
+  argmax_step<32>(v, i);
+}
+
+// Lane l receives lane l-1's value; lane 0 receives `first`.
+__device__ __forceinline__ int shift_up1(int v, int first) { return dpp<0x138>(v, first); }
+__device__ __forceinline__ float shift_up1(float v, float first) {
+  return __builtin_bit_cast(float, dpp<0x138>(__builtin_bit_cast(int, v), __builtin_bit_cast(int, first)));
+}
+
+// Bitonic sort of one (value, id) pair per lane into `better` order (lane 0 best).
+__device__ __forceinline__ void wave_sort(float& v, int& id) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j >= 1; j >>= 1) {
+      const float pv = __shfl_xor(v, j);
+      const int pi = __shfl_xor(id, j);
+      const bool here = ((lane & j) == 0) == ((lane & k) == 0);  // keep the better one here
+      const bool take = here ? better(pv, pi, v, id) : better(v, id, pv, pi);
+      if (take) {
+        v = pv;
+        id = pi;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- device properties

@@ -6,15 +6,17 @@
 // log q = logit - logsumexp(row).
 //
 // Two kernels, both HBM-streaming:
-//   topk_partial  grid (chunks, rows), 256 threads.  Each wave streams an
-//                 interleaved part of one chunk with 16-byte loads, keeping
+//   topk_partial  one 256-thread workgroup per (row, chunk).  Each wave streams an
+//                 interleaved part of the chunk with 16-byte loads, keeping
 //                 (a) a running max and an fp64 sum of exp(x - max) per lane, and
-//                 (b) a sorted top-K list spread over the wave, lane i holding
-//                 the i-th best.  A value enters the list only if it beats the
-//                 current K-th entry, which after the first few hundred elements
-//                 is rare, so the stream runs at load rate.
-//   topk_merge    one wave per row merges the lists and statistics of all
-//                 chunks and writes tokens and log-probabilities.
+//                 (b) a sorted top-K list spread over the wave, lane i holding the
+//                 i-th best.  The list starts as a bitonic sort of the first 64
+//                 values; after that a value enters only if it beats the K-th
+//                 entry, which is rare, and enters by a one-lane DPP shift.  The
+//                 four waves' lists and sums are merged in LDS, one result per
+//                 workgroup.
+//   topk_merge    one wave per row merges the chunks' lists and sums and writes
+//                 tokens and log-probabilities.
 #include <float.h>
 #include <limits.h>
 
@@ -40,11 +42,13 @@ struct TopList {
   float thr_val;  // k-th best so far (uniform)
   int thr_id;
 
-  __device__ void init() {
-    val = -INFINITY;
-    id = INT_MAX;
-    thr_val = -INFINITY;
-    thr_id = INT_MAX;
+  // Start from one value per lane (invalid lanes contribute nothing).
+  __device__ void seed(float v, int i, bool valid, int k) {
+    val = valid ? v : -INFINITY;
+    id = valid ? i : INT_MAX;
+    wave_sort(val, id);
+    thr_val = readlane(val, k - 1);
+    thr_id = readlane(id, k - 1);
   }
 
   // Insert the uniform candidate (v, i) if it beats the k-th entry.
@@ -53,8 +57,8 @@ struct TopList {
     const int lane = lane_id();
     const bool ahead = lane < k && better(val, id, v, i);
     const int pos = __popcll(ballot(ahead));
-    const float up_v = __shfl_up(val, 1);
-    const int up_i = __shfl_up(id, 1);
+    const float up_v = shift_up1(val, -INFINITY);
+    const int up_i = shift_up1(id, INT_MAX);
     if (lane > pos) {
       val = up_v;
       id = up_i;
@@ -67,7 +71,7 @@ struct TopList {
     thr_id = readlane(id, k - 1);
   }
 
-  // Offer one value per lane; candidates are inserted one at a time.
+  // Offer one value per lane; the (few) qualifying ones are inserted one by one.
   __device__ void offer(float v, int i, bool valid, int k) {
     unsigned long long m = ballot(valid && better(v, i, thr_val, thr_id));
     while (m) {
@@ -78,24 +82,39 @@ struct TopList {
   }
 };
 
-__device__ __forceinline__ void stat_add4(float& m, double& s, float x0, float x1, float x2,
-                                          float x3) {
-  const float mx = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+__device__ __forceinline__ void stat_add4(float& m, double& s, const float (&x)[4]) {
+  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   if (mx > m) {
     s = (m == -INFINITY) ? 0.0 : s * exp2((double)(m - mx) * (double)kLog2e);
     m = mx;
   }
-  if (m == -INFINITY) return;  // nothing valid seen yet (ragged tail)
-  const float e = __builtin_amdgcn_exp2f((x0 - m) * kLog2e) + __builtin_amdgcn_exp2f((x1 - m) * kLog2e) +
-                  __builtin_amdgcn_exp2f((x2 - m) * kLog2e) + __builtin_amdgcn_exp2f((x3 - m) * kLog2e);
+  if (m == -INFINITY) return;  // nothing valid seen yet
+  const float e = __builtin_amdgcn_exp2f((x[0] - m) * kLog2e) + __builtin_amdgcn_exp2f((x[1] - m) * kLog2e) +
+                  __builtin_amdgcn_exp2f((x[2] - m) * kLog2e) + __builtin_amdgcn_exp2f((x[3] - m) * kLog2e);
   s += (double)e;
 }
 
+// Merge (m, s) pairs: returns the pair for the union.
+__device__ __forceinline__ void stat_merge(float& m, double& s, float m2, double s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float mx = fmaxf(m, m2);
+  s = s * exp2((double)(m - mx) * (double)kLog2e) + s2 * exp2((double)(m2 - mx) * (double)kLog2e);
+  m = mx;
+}
+
 __global__ void __launch_bounds__(kThreads)
-topk_partial(const float* __restrict__ logits, int64_t rows, int64_t stride, int vocab, int k,
+topk_partial(const float* __restrict__ logits, int nchunks, int64_t stride, int vocab, int k,
              int64_t chunk_len, bool vec_ok, float* __restrict__ cand_val,
              int* __restrict__ cand_id, Stat* __restrict__ stats) {
-  const int nchunks = (int)(gridDim.x / rows);
+  __shared__ float lv[kWavesPerBlock][kWave];
+  __shared__ int li[kWavesPerBlock][kWave];
+  __shared__ float lm[kWavesPerBlock];
+  __shared__ double ls[kWavesPerBlock];
   const int c = (int)(blockIdx.x % nchunks);
   const int64_t row = blockIdx.x / nchunks;
   const int tid = threadIdx.x;
@@ -104,45 +123,65 @@ topk_partial(const float* __restrict__ logits, int64_t rows, int64_t stride, int
   const float* x = logits + row * stride;
   const int lo = (int)(c * chunk_len);
   const int hi = (int)min<int64_t>((int64_t)lo + chunk_len, vocab);
+  const int niter = (hi - lo + kThreads * 4 - 1) / (kThreads * 4);  // uniform over the block
 
   TopList list;
-  list.init();
   float m = -INFINITY;
   double s = 0.0;
-
-  int base = lo + tid * 4;
-  if (vec_ok) {
-    for (; base + 3 < hi; base += kThreads * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(x + base);
-      stat_add4(m, s, v.x, v.y, v.z, v.w);
-      list.offer(v.x, base + 0, true, k);
-      list.offer(v.y, base + 1, true, k);
-      list.offer(v.z, base + 2, true, k);
-      list.offer(v.w, base + 3, true, k);
+  for (int it = 0; it < niter; ++it) {
+    const int base = lo + (it * kThreads + tid) * 4;
+    float v[4];
+    if (vec_ok && base + 3 < hi) {
+      const float4 t = *reinterpret_cast<const float4*>(x + base);
+      v[0] = t.x;
+      v[1] = t.y;
+      v[2] = t.z;
+      v[3] = t.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (base + j < hi) ? x[base + j] : -INFINITY;
+    }
+    stat_add4(m, s, v);
+    if (it == 0) {
+      list.seed(v[0], base, base < hi, k);
+#pragma unroll
+      for (int j = 1; j < 4; ++j) list.offer(v[j], base + j, base + j < hi, k);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) list.offer(v[j], base + j, base + j < hi, k);
     }
   }
-  // scalar path (unaligned rows) and the ragged tail
-  for (; base < hi; base += kThreads * 4) {
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = (base + j < hi) ? x[base + j] : -INFINITY;
-    stat_add4(m, s, v[0], v[1], v[2], v[3]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) list.offer(v[j], base + j, base + j < hi, k);
-  }
-  // lanes that never saw a value keep m = -inf, s = 0
+  // per-wave results to LDS
   const float wm = wave_max(m);
   const double ws = wave_sum(m == -INFINITY ? 0.0 : s * exp2((double)(m - wm) * (double)kLog2e));
-  const int64_t slot = (row * nchunks + c) * kWavesPerBlock + wave;
+  lv[wave][lane] = lane < k ? list.val : -INFINITY;
+  li[wave][lane] = lane < k ? list.id : INT_MAX;
+  if (lane == 0) {
+    lm[wave] = wm;
+    ls[wave] = ws;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // wave 0 folds in the other waves' lists and sums
+  float fm = lm[0];
+  double fs = ls[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) stat_merge(fm, fs, lm[w], ls[w]);
+  for (int w = 1; w < kWavesPerBlock; ++w) {
+    const float v = lv[w][lane];
+    const int i = li[w][lane];
+    list.offer(v, i, lane < k && i != INT_MAX, k);
+  }
+  const int64_t slot = row * nchunks + c;
   if (lane < k) {
     cand_val[slot * k + lane] = list.val;
     cand_id[slot * k + lane] = list.id;
   }
   if (lane == 0) {
     Stat st;
-    st.m = wm;
+    st.m = fm;
     st.pad = 0.f;
-    st.s = ws;
+    st.s = fs;
     stats[slot] = st;
   }
 }
@@ -155,29 +194,37 @@ topk_merge(int nlists, int k, const float* __restrict__ cand_val, const int* __r
   const int lane = threadIdx.x;
   const Stat* st = stats + row * nlists;
 
-  // log-sum-exp over lists, fp64
+  // log-sum-exp over the chunks, fp64
   float m = -INFINITY;
-  for (int i = lane; i < nlists; i += kWave) m = fmaxf(m, st[i].m);
-  const float M = wave_max(m);
   double s = 0.0;
   for (int i = lane; i < nlists; i += kWave) {
     const Stat t = st[i];
-    if (t.m != -INFINITY) s += t.s * exp2((double)(t.m - M) * (double)kLog2e);
+    stat_merge(m, s, t.m, t.s);
   }
-  s = wave_sum(s);
+  const float M = wave_max(m);
+  s = wave_sum(m == -INFINITY ? 0.0 : s * exp2((double)(m - M) * (double)kLog2e));
   const double lse = (double)M + log(s);
 
+  const int n = nlists * k;
+  const float* cv = cand_val + row * (int64_t)n;
+  const int* ci = cand_id + row * (int64_t)n;
   TopList list;
-  list.init();
-  const int64_t n = (int64_t)nlists * k;
-  const float* cv = cand_val + row * n;
-  const int* ci = cand_id + row * n;
-  for (int64_t b = 0; b < n; b += kWave) {
-    const int64_t i = b + lane;
-    const bool valid = i < n;
-    const float v = valid ? cv[i] : -INFINITY;
-    const int id = valid ? ci[i] : INT_MAX;
-    list.offer(v, id, valid && id != INT_MAX, k);
+  {
+    const bool valid = lane < n;
+    list.seed(valid ? cv[lane] : -INFINITY, valid ? ci[lane] : INT_MAX, valid && ci[lane] != INT_MAX, k);
+  }
+  constexpr int kBatch = 4;  // batches loaded together, so their loads overlap
+  for (int b0 = kWave; b0 < n; b0 += kBatch * kWave) {
+    float v[kBatch];
+    int id[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = b0 + j * kWave + lane;
+      v[j] = i < n ? cv[i] : -INFINITY;
+      id[j] = i < n ? ci[i] : INT_MAX;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) list.offer(v[j], id[j], id[j] != INT_MAX, k);
   }
   if (lane < k) {
     out_tok[row * k + lane] = list.id;
@@ -196,7 +243,7 @@ TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   nch = ceil_div(vocab, len);
   p.nchunks = (int)nch;
   p.chunk_len = len;
-  const size_t nslot = (size_t)rows * nch * kWavesPerBlock;
+  const size_t nslot = (size_t)rows * nch;
   p.ws_bytes = align_up(nslot * k * sizeof(float), 256) + align_up(nslot * k * sizeof(int), 256) +
                align_up(nslot * sizeof(Stat), 256);
   return p;
@@ -204,7 +251,7 @@ TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
 
 hipError_t launch_topk(const float* logits, int64_t rows, int64_t vocab, int64_t stride, int k,
                        int32_t* tok, float* logq, void* ws, const TopkPlan& plan, hipStream_t st) {
-  const size_t nslot = (size_t)rows * plan.nchunks * kWavesPerBlock;
+  const size_t nslot = (size_t)rows * plan.nchunks;
   char* w = static_cast<char*>(ws);
   float* cv = reinterpret_cast<float*>(w);
   w += align_up(nslot * k * sizeof(float), 256);
@@ -213,11 +260,12 @@ hipError_t launch_topk(const float* logits, int64_t rows, int64_t vocab, int64_t
   Stat* stt = reinterpret_cast<Stat*>(w);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && (stride % 4 == 0);
   hipLaunchKernelGGL(topk_partial, dim3((unsigned)(plan.nchunks * rows)), dim3(kThreads), 0, st,
-                     logits, rows, stride, (int)vocab, k, plan.chunk_len, vec_ok, cv, ci, stt);
+                     logits, plan.nchunks, stride, (int)vocab, k, plan.chunk_len, vec_ok, cv, ci,
+                     stt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(kWave), 0, st,
-                     plan.nchunks * kWavesPerBlock, k, cv, ci, stt, tok, logq);
+  hipLaunchKernelGGL(topk_merge, dim3((unsigned)rows), dim3(kWave), 0, st, plan.nchunks, k, cv, ci,
+                     stt, tok, logq);
   return hipGetLastError();
 }
 

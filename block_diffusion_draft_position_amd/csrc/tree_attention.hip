@@ -60,7 +60,9 @@ struct Unit {
 
 // Workgroup -> (unit, row group).  Row groups of one unit are 8 workgroups apart,
 // so they land on the same XCD (workgroups are dealt to the 8 XCDs round robin)
-// and share that XCD's L2 for the unit's K/V.
+// and share that XCD's L2 for the unit's K/V.  The split index varies slowest, so
+// consecutive units are different (sequence, KV head) pairs of equal kind and the
+// prefix splits spread over all XCDs (tree splits, which are short, come last).
 __device__ __forceinline__ bool decode_block(int Hkv, int nsplit_tot, int row_groups, int units,
                                              Unit& u) {
   const int blk = blockIdx.x;
@@ -69,8 +71,9 @@ __device__ __forceinline__ bool decode_block(int Hkv, int nsplit_tot, int row_gr
   u.rg = rest % row_groups;
   const int un = (rest / row_groups) * 8 + x8;
   if (un >= units) return false;
-  u.c = un % nsplit_tot;
-  const int sg = un / nsplit_tot;
+  const int nsg = units / nsplit_tot;  // sequences x KV heads
+  u.c = un / nsg;
+  const int sg = un % nsg;
   u.g = sg % Hkv;
   u.s = sg / Hkv;
   return true;
@@ -308,6 +311,339 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   }
 }
 
+// ---------------------------------------------------------------- bf16, D = 128 (gfx950 path)
+// Same decomposition as attn_partial_bf16, rebuilt around gfx950 features:
+//   * K and V tiles (64 keys) go global -> LDS with global_load_lds_dwordx4, no
+//     registers in between, into a 4-stage ring: three tiles are in flight while
+//     one is consumed, and one barrier per tile suffices (the stage being refilled
+//     was consumed one barrier earlier).  A 256-byte key row keeps its sixteen
+//     16-byte chunks XOR-swizzled (chunk c of key k at slot c ^ swz(k)) so that
+//     both the K reads and the transposed V reads are free of bank conflicts.
+//   * V stays row-major; the PV operand V^T is read with ds_read_b64_tr_b16, which
+//     hands each lane of a 16-lane group one head-dim column of a 4-key block.
+//   * v_mfma_f32_16x16x32_bf16 with 32 query rows per wave (two 16-row blocks that
+//     share every K/V fragment read from LDS).
+//   * The running max is raised only when a tile's max exceeds it by more than
+//     2^8; otherwise O and l are not rescaled (p <= 2^8 stays exact in fp32/bf16).
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void glob_void;
+
+constexpr int kStages = 4;
+constexpr int kTileBytes = kTile * 128 * 2;      // one K or V tile, D = 128
+constexpr float kTau = 8.f;                      // lazy-rescale slack (base-2 units)
+
+// The ring: one statically allocated K and V buffer per stage.  Separate objects let
+// the compiler see that a stage being read does not alias the stages still being
+// filled, so it keeps the explicit per-stage vmcnt waits instead of draining all
+// outstanding loads before every LDS read.
+__shared__ __align__(16) unsigned char g_ring_k0[kTileBytes], g_ring_v0[kTileBytes];
+__shared__ __align__(16) unsigned char g_ring_k1[kTileBytes], g_ring_v1[kTileBytes];
+__shared__ __align__(16) unsigned char g_ring_k2[kTileBytes], g_ring_v2[kTileBytes];
+__shared__ __align__(16) unsigned char g_ring_k3[kTileBytes], g_ring_v3[kTileBytes];
+
+template <int ST>
+__device__ __forceinline__ unsigned char* ring_k() {
+  if constexpr (ST == 0) return g_ring_k0;
+  if constexpr (ST == 1) return g_ring_k1;
+  if constexpr (ST == 2) return g_ring_k2;
+  if constexpr (ST == 3) return g_ring_k3;
+}
+template <int ST>
+__device__ __forceinline__ unsigned char* ring_v() {
+  if constexpr (ST == 0) return g_ring_v0;
+  if constexpr (ST == 1) return g_ring_v1;
+  if constexpr (ST == 2) return g_ring_v2;
+  if constexpr (ST == 3) return g_ring_v3;
+}
+
+// Slot swizzle of a key row (a bijection on 0..15): the sixteen K rows read by one
+// 16-lane group land in sixteen different 16-byte slots, and the four rows of a
+// transposed V read get slot offsets that differ in bits 1-3 with bit 0 equal, so
+// with the two chunks (c, c ^ 1) they fill sixteen different slots per 32 lanes.
+// (Measured: a variant aimed at 32 banks doubled the bank-conflict cycles.)
+__device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
+attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
+          const bf16_t* __restrict__ vc, const int64_t* __restrict__ cu_prefix,
+          const bf16_t* __restrict__ kt, const bf16_t* __restrict__ vt,
+          const uint32_t* __restrict__ mask, const int32_t* __restrict__ num_nodes,
+          int N, int Hq, int Hkv, int G, int R, int W, int rows_pad, int nsplit,
+          int64_t chunk, int units, int row_groups, float scale_log2,
+          float* __restrict__ opart, float2* __restrict__ mlpart) {
+  constexpr int D = 128;
+  constexpr int NLOAD = (32 + NW - 1) / NW;  // 1 KB load instructions per wave per tile
+
+  Unit u;
+  if (!decode_block(Hkv, nsplit + 1, row_groups, units, u)) return;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int g4 = lane / 16;   // 16-lane group
+  const int l16 = lane % 16;
+
+  const int nn = num_nodes[u.s];
+  const int64_t p0 = cu_prefix[u.s];
+  const int64_t P = kc ? cu_prefix[u.s + 1] - p0 : 0;
+  const int64_t kstride = (int64_t)Hkv * D;
+  const bool tree = u.c == nsplit;
+  int64_t lo, hi;
+  const bf16_t* kb;
+  const bf16_t* vb;
+  if (!tree) {
+    const int64_t nvalid = P > 0 ? min<int64_t>(nsplit, (P + chunk - 1) / chunk) : 0;
+    if (u.c >= nvalid) return;
+    lo = (int64_t)u.c * chunk;
+    hi = (u.c == nvalid - 1) ? P : lo + chunk;
+    kb = kc + (p0 * Hkv + u.g) * D;
+    vb = vc + (p0 * Hkv + u.g) * D;
+  } else {
+    lo = 0;
+    hi = nn;
+    kb = kt + ((int64_t)u.s * N * Hkv + u.g) * D;
+    vb = vt + ((int64_t)u.s * N * Hkv + u.g) * D;
+  }
+  const int ntiles = (int)((hi - lo + kTile - 1) / kTile);
+
+  // ---- the loads of tile t into ring stage ST: 32 instructions of 1 KB (4 key rows),
+  // 16 for K then 16 for V, dealt round robin to the waves.  Rows past the split
+  // (last tile) re-read the split's last row and are masked later.
+  auto issue = [&]<int ST>(int t) {
+    const int64_t t0 = lo + (int64_t)t * kTile;
+    const bool full = t0 + kTile <= hi;
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) {
+      const int i = (wave + j * NW) & 31;
+      const bool isv = i >= 16;
+      const bf16_t* base = (isv ? vb : kb) + t0 * kstride;
+      int key = 4 * (i & 15) + g4;
+      const int c = l16 ^ swz(key);
+      if (!full) key = min(key, (int)(hi - 1 - t0));
+      const int off = key * (int)kstride + c * 8;
+      unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + (i & 15) * 1024;
+      __builtin_amdgcn_global_load_lds((glob_void*)(base + off), (lds_void*)dst, 16, 0, 0);
+    }
+  };
+
+  // ---- this lane's two query rows (blocks of 16) and their Q fragments (B operand)
+  int rowq[2], nodeq[2];
+  bool okq[2];
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    rowq[qb] = (u.rg * NW + wave) * 32 + qb * 16 + l16;
+    nodeq[qb] = rowq[qb] / G;
+    okq[qb] = rowq[qb] < R && nodeq[qb] < nn;
+    const int head = u.g * G + (rowq[qb] % G);
+    const bf16_t* qrow = q + (((int64_t)u.s * N + nodeq[qb]) * Hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[qb][kk] = okq[qb] ? *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + g4 * 8) : bf16x8{};
+  }
+  const uint32_t* mrow0 = mask + ((int64_t)u.s * N + (okq[0] ? nodeq[0] : 0)) * W;
+  const uint32_t* mrow1 = mask + ((int64_t)u.s * N + (okq[1] ? nodeq[1] : 0)) * W;
+
+  // per-lane LDS read offsets (see the reads below)
+  int kofs[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kofs[kk] = l16 * 256 + (((4 * kk + g4) ^ swz(l16)) << 4);
+  const int vrow = 4 * g4 + l16 / 4;   // key row within a 32-key half (and +16)
+  const int vsw = swz(vrow);
+  const int vsw_hi = vsw & 14;
+  const int vsw_lo = ((l16 & 3) >> 1) ^ (vsw & 1);
+  const int vbase = vrow * 256 + (l16 & 1) * 8;
+
+  f32x4 oacc[2][8];
+  f32x4 lacc[2];  // row sums of P, from an MFMA against an all-ones block
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[qb][db] = f32x4{};
+    lacc[qb] = f32x4{};
+  }
+  float m_run[2] = {-INFINITY, -INFINITY};
+  bf16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (bf16_t)1.f;
+
+  // ---- one tile from ring stage ST
+  auto step = [&]<int ST>(int t) {
+    // wait for this wave's loads of tile t (tiles t+1, t+2 may stay in flight).
+    // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at max.
+    constexpr int kV1 = NLOAD < 63 ? NLOAD : 63;
+    constexpr int kV2 = 2 * NLOAD < 63 ? 2 * NLOAD : 63;
+    const int ahead = min(ntiles - 1 - t, kStages - 2);
+    if (tree || ahead <= 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt((kV1 & 0xf) | ((kV1 >> 4) << 14) | 0x0f70);
+    else __builtin_amdgcn_s_waitcnt((kV2 & 0xf) | ((kV2 >> 4) << 14) | 0x0f70);
+    // execution barrier only: every wave has waited for its own loads of tile t
+    // (a __syncthreads fence would also drain the tiles still in flight); the stage
+    // refilled next was read one barrier ago
+    __builtin_amdgcn_s_barrier();
+    if (t + kStages - 1 < ntiles) issue.template operator()<(ST + kStages - 1) % kStages>(t + kStages - 1);
+
+    // Per-lane offsets are re-materialised in every step (an empty asm hides their
+    // loop invariance); otherwise the compiler keeps one copy per ring stage live.
+    int kof[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      kof[kk] = kofs[kk];
+      asm volatile("" : "+v"(kof[kk]));
+    }
+    int vb_ = vbase, vhi = vsw_hi, vlo = vsw_lo;
+    asm volatile("" : "+v"(vb_), "+v"(vhi), "+v"(vlo));
+    const unsigned char* Ks = ring_k<ST>();
+    const unsigned char* Vs = ring_v<ST>();
+    const int64_t t0 = lo + (int64_t)t * kTile;
+    const int rem = (int)(hi - lo) - t * kTile;  // keys left in the split; masks apply if < 64
+
+    // ---- S^T = K . Q^T  (4 key blocks x 2 query blocks).  Key kb4*16 + l16 has the
+    // swizzle of l16, so the lane's read offsets are kofs[kk] + kb4 * 4096.
+    f32x4 sacc[2][4];
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kof[kk] + kb4 * 4096);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[qb][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][kk],
+                                                                  kk == 0 ? f32x4{} : sacc[qb][kb4], 0, 0, 0);
+      }
+      if (kb4 & 1) __builtin_amdgcn_sched_barrier(0);  // at most 8 K fragments live
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: bounded register use
+    // ---- masks: ragged tail, and in the tree split the ancestor bits
+    if (tree) {
+      // bit (kin) of the two 32-key words; this lane's keys are kb4*16 + 4*g4 + r
+      const int wi = (int)(t0 >> 5);
+      uint32_t w[2][2];
+      w[0][0] = wi < W ? mrow0[wi] : 0u;
+      w[0][1] = wi + 1 < W ? mrow0[wi + 1] : 0u;
+      w[1][0] = wi < W ? mrow1[wi] : 0u;
+      w[1][1] = wi + 1 < W ? mrow1[wi + 1] : 0u;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+          const uint32_t bits = w[qb][kb4 >> 1] >> ((kb4 & 1) * 16 + g4 * 4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb4 * 16 + g4 * 4 + r >= rem || !((bits >> r) & 1u)) sacc[qb][kb4][r] = -INFINITY;
+        }
+    } else if (rem < kTile) {
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kb4 * 16 + g4 * 4 + r >= rem) {
+            sacc[0][kb4][r] = -INFINITY;
+            sacc[1][kb4][r] = -INFINITY;
+          }
+    }
+    // ---- online softmax (base 2), lazy rescale
+    bool need[2];
+    float tmax[2], m_use[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+        mx = fmaxf(mx, fmaxf(fmaxf(sacc[qb][kb4][0], sacc[qb][kb4][1]), fmaxf(sacc[qb][kb4][2], sacc[qb][kb4][3])));
+      mx = fmaxf(mx, xchg<16>(mx));
+      mx = fmaxf(mx, xchg<32>(mx));
+      tmax[qb] = mx * scale_log2;
+      need[qb] = tmax[qb] > m_run[qb] + kTau;   // always true on the first unmasked tile
+    }
+    if (ballot(need[0] || need[1])) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = need[qb] ? tmax[qb] : m_run[qb];
+        const float alpha = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        lacc[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[qb][db] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb4][r], scale_log2, -m_use[qb]));
+          pb[qb][kb4 / 2][(kb4 & 1) * 4 + r] = (bf16_t)p;
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T . P^T  (V^T read transposed from the row-major tile).  The two
+    // key rows a lane addresses (vrow, vrow + 16, plus 32 per key half) share one
+    // swizzle, so the chunk slot is (2 db) ^ vsw_hi | vsw_lo.
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int slot = (((2 * db) ^ vhi) | vlo) << 4;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const unsigned char* p = Vs + vb_ + kh * 32 * 256 + slot;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * 256));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qb][kh], oacc[qb][db], 0, 0, 0);
+      }
+      if (db & 1) __builtin_amdgcn_sched_barrier(0);  // at most 8 V fragments live
+    }
+    // sum_k P[k][q] for every query: the same contraction with V replaced by ones
+    // (the sum is of the bf16 weights the numerator uses)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][kh], lacc[qb], 0, 0, 0);
+  };
+
+  // prologue: tiles 0..2 in flight
+  if (0 < ntiles) issue.template operator()<0>(0);
+  if (1 < ntiles) issue.template operator()<1>(1);
+  if (2 < ntiles) issue.template operator()<2>(2);
+  // tile t uses stage t % 4; the loop is unrolled by the ring depth so every stage is
+  // a distinct object at compile time
+  if (0 < ntiles) step.template operator()<0>(0);
+  for (int t = 1; t < ntiles; t += 2 * kStages) {
+    step.template operator()<1>(t);
+    if (t + 1 < ntiles) step.template operator()<2>(t + 1);
+    if (t + 2 < ntiles) step.template operator()<3>(t + 2);
+    if (t + 3 < ntiles) step.template operator()<0>(t + 3);
+    if (t + 4 < ntiles) step.template operator()<1>(t + 4);
+    if (t + 5 < ntiles) step.template operator()<2>(t + 5);
+    if (t + 6 < ntiles) step.template operator()<3>(t + 6);
+    if (t + 7 < ntiles) step.template operator()<0>(t + 7);
+  }
+
+  // ---- partial results of this split
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = lacc[qb][0];
+    if (rowq[qb] < R) {
+      const int64_t urow = (((int64_t)u.s * Hkv + u.g) * (nsplit + 1) + u.c) * rows_pad + rowq[qb];
+      float* orow = opart + urow * D;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<float4*>(orow + db * 16 + g4 * 4) =
+            make_float4(oacc[qb][db][0], oacc[qb][db][1], oacc[qb][db][2], oacc[qb][db][3]);
+      if (g4 == 0) mlpart[urow] = make_float2(m_run[qb], lt);
+    }
+  }
+}
+
 // Merge the splits of each row: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
 template <typename OutT, int D>
 __global__ void __launch_bounds__(256)
@@ -474,6 +810,36 @@ hipError_t launch_partial(const AttnPlan& p, const void* q, const void* kc, cons
   return hipGetLastError();
 }
 
+template <int NW>
+hipError_t launch_d128_nw(const AttnPlan& p, const void* q, const void* kc, const void* vc,
+                          const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
+                          const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
+                          float* opart, float2* ml, hipStream_t st) {
+  const int units = S * Hkv * (p.nsplit + 1);
+  const int blocks = (int)(ceil_div(units, 8) * 8 * p.row_groups);
+  hipLaunchKernelGGL((attn_d128<NW>), dim3(blocks), dim3(NW * 64), 0, st, (const bf16_t*)q,
+                     (const bf16_t*)kc, (const bf16_t*)vc, cu, (const bf16_t*)kt, (const bf16_t*)vt,
+                     mask, nn, N, Hq, Hkv, p.G, p.R, W, p.rows_pad, p.nsplit, p.chunk, units,
+                     p.row_groups, scale * kLog2e, opart, ml);
+  return hipGetLastError();
+}
+
+hipError_t launch_d128(const AttnPlan& p, const void* q, const void* kc, const void* vc,
+                       const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
+                       const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
+                       float* opart, float2* ml, hipStream_t st) {
+#define DDT_NW(X)                                                                            \
+  case X:                                                                                    \
+    return launch_d128_nw<X>(p, q, kc, vc, cu, kt, vt, mask, nn, S, N, Hq, Hkv, W, scale,   \
+                             opart, ml, st);
+  switch (p.waves) {
+    DDT_NW(1) DDT_NW(2) DDT_NW(3) DDT_NW(4) DDT_NW(5) DDT_NW(6) DDT_NW(7) DDT_NW(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef DDT_NW
+}
+
 template <int D>
 hipError_t launch_partial_d(const AttnPlan& p, const void* q, const void* kc, const void* vc,
                             const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
@@ -509,16 +875,23 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_
     p.ws_bytes = 0;
     return p;
   }
-  const int tiles = (int)ceil_div(p.R, 32);
-  p.row_groups = (int)ceil_div(tiles, 8);
-  p.waves = (int)ceil_div(tiles, p.row_groups);
+  if (D == 128) {
+    // attn_d128: 32 rows per wave, up to 8 waves per workgroup (more would spill)
+    const int waves = (int)ceil_div(ceil_div(p.R, 16), 2);
+    p.row_groups = (int)ceil_div(waves, 8);
+    p.waves = (int)ceil_div(waves, p.row_groups);
+  } else {
+    const int tiles = (int)ceil_div(p.R, 32);
+    p.row_groups = (int)ceil_div(tiles, 8);
+    p.waves = (int)ceil_div(tiles, p.row_groups);
+  }
   p.rows_pad = p.row_groups * p.waves * 32;
   const int64_t units_base = (int64_t)S * Hkv * p.row_groups;
   const int64_t target = 2 * (int64_t)cu_count();
   const int64_t maxp = std::max<int64_t>(max_prefix, 0);
   const int64_t want = std::max<int64_t>(1, ceil_div(target, units_base));
   int64_t chunk = (int64_t)align_up((size_t)std::max<int64_t>(1, ceil_div(maxp, want)), kTile);
-  chunk = std::max<int64_t>(chunk, 2 * kTile);
+  chunk = std::max<int64_t>(chunk, (D == 128 ? 4 : 2) * kTile);
   p.chunk = chunk;
   p.nsplit = (int)std::max<int64_t>(1, ceil_div(maxp, chunk));
   const size_t rows = (size_t)S * Hkv * (p.nsplit + 1) * p.rows_pad;
@@ -556,7 +929,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   switch (D) {
     case 32: e = launch_partial_d<32>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st); break;
     case 64: e = launch_partial_d<64>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st); break;
-    case 128: e = launch_partial_d<128>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st); break;
+    case 128: e = launch_d128(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

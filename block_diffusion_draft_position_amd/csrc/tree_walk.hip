@@ -29,16 +29,6 @@ __device__ __forceinline__ void take(ArgMax& a, float v, int i) {
   }
 }
 
-__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float v = __shfl_xor(a.v, o);
-    const int i = __shfl_xor(a.i, o);
-    take(a, v, i);
-  }
-  return a;
-}
-
 __global__ void __launch_bounds__(kThreads)
 argmax_partial(const float* __restrict__ target, const int32_t* __restrict__ num_nodes, int N,
                int vocab, int nchunks, int64_t chunk_len, bool vec_ok,
@@ -55,19 +45,18 @@ argmax_partial(const float* __restrict__ target, const int32_t* __restrict__ num
   const int hi = (int)min<int64_t>((int64_t)lo + chunk_len, vocab);
   const int tid = threadIdx.x;
   ArgMax a{-INFINITY, INT_MAX};
-  int base = lo + tid * 4;
-  if (vec_ok) {
-    for (; base + 3 < hi; base += kThreads * 4) {
+  for (int base = lo + tid * 4; base < hi; base += kThreads * 4) {
+    if (vec_ok && base + 3 < hi) {
       const float4 v = *reinterpret_cast<const float4*>(x + base);
       take(a, v.x, base);
       take(a, v.y, base + 1);
       take(a, v.z, base + 2);
       take(a, v.w, base + 3);
+    } else {
+      for (int j = 0; j < 4 && base + j < hi; ++j) take(a, x[base + j], base + j);
     }
   }
-  for (; base < hi; base += kThreads * 4)
-    for (int j = 0; j < 4 && base + j < hi; ++j) take(a, x[base + j], base + j);
-  a = wave_argmax(a);
+  wave_argmax(a.v, a.i);
   if (tid % kWave == 0) red[tid / kWave] = a;
   __syncthreads();
   if (tid == 0) {
@@ -81,19 +70,22 @@ walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ pa
             const int32_t* __restrict__ num_nodes, const ArgMax* __restrict__ part, int N, int L,
             int nchunks, int32_t* __restrict__ accept_len, int32_t* __restrict__ acc_nodes,
             int32_t* __restrict__ acc_tok, int32_t* __restrict__ bonus_out) {
-  extern __shared__ int want[];  // [N] target's greedy token at each node
+  extern __shared__ int smem[];
+  int* want = smem;          // [N] target's greedy token at each node
+  int* tok = smem + N;       // [N]
+  int* par = smem + 2 * N;   // [N]
   const int s = blockIdx.x;
   const int lane = threadIdx.x;
   const int nn = num_nodes[s];
   for (int n = lane; n < nn; n += kWave) {
+    tok[n] = tree_tok[(int64_t)s * N + n];
+    par[n] = parent[(int64_t)s * N + n];
     const ArgMax* p = part + ((int64_t)s * N + n) * nchunks;
     ArgMax a = p[0];
     for (int c = 1; c < nchunks; ++c) take(a, p[c].v, p[c].i);
     want[n] = a.i;
   }
   __syncthreads();
-  const int32_t* tok = tree_tok + (int64_t)s * N;
-  const int32_t* par = parent + (int64_t)s * N;
   int cur = 0;
   int a = 0;
   while (a < L) {
@@ -152,7 +144,7 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                      num_nodes, N, (int)vocab, plan.nchunks, plan.chunk_len, vec_ok, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(walk_kernel, dim3(S), dim3(kWave), sizeof(int) * N, st, tree_tok, parent,
+  hipLaunchKernelGGL(walk_kernel, dim3(S), dim3(kWave), 3 * sizeof(int) * N, st, tree_tok, parent,
                      num_nodes, part, N, L, plan.nchunks, accept_len, acc_nodes, acc_tok,
                      bonus_out);
   return hipGetLastError();

@@ -17,7 +17,8 @@ from ddt_synthetic.configs import Config
 #   attention fp32: per row max|d| <= 1e-5 * max|ref|.
 #   attention bf16: |d| <= 2e-2 + 1e-2 |ref| elementwise, and per row
 #     ||d||_2 <= 1e-2 ||ref||_2 (an all-zero output would pass the first alone).
-#   lse: 1e-5 (fp32 inputs) / 1e-3 (bf16 inputs) absolute.
+#   lse: 1e-5 (fp32 inputs); 4e-3 for bf16 inputs, whose row sums are formed from the
+#     bf16-rounded softmax weights (relative error <= 2^-8 in the sum).
 TOPK_ATOL = 2e-5
 NODE_LOGQ_ATOL = 1e-4
 F32_ROW_RTOL = 1e-5

@@ -108,7 +108,7 @@ def run_case(cfg, att=None, rows_per_seq=None, sharp=False, seed_rows=0):
         check_attention_rows(go[idx_n, idx_h], ref_o, cfg.dtype, f"{cfg.name} seq {s}")
         valid = idx_n < nn
         np.testing.assert_allclose(gl[idx_n[valid], idx_h[valid]], ref_l[valid], rtol=0,
-                                   atol=1e-5 if cfg.dtype == "f32" else 1e-3)
+                                   atol=1e-5 if cfg.dtype == "f32" else 4e-3)
         assert np.all(np.isneginf(gl[idx_n[~valid], idx_h[~valid]]))
     return gw
 
