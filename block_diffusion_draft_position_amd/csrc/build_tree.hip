@@ -1,27 +1,28 @@
-// Draft-tree construction under a node budget: best-first selection of the B most
-// probable draft prefixes (DDTree page "策展 · X (Twitter)": section 核心創新 for the
-// best-first heap and budget, 運作流程 step 2 for the construction, 理論基礎 for
-// the factorised prefix probability and the prefix-closure of the optimum).
+// Draft-tree construction under a node budget: the B most probable draft prefixes
+// (DDTree page "策展 · X (Twitter)": section 核心創新 for the best-first selection
+// under a budget, 運作流程 step 2 for the construction, 理論基礎 for the factorised
+// prefix probability and the prefix-closure of the optimum).
 //
-// One wavefront per sequence.  The candidate prefixes form a K-ary tree whose
-// depth-i children are position i's top-K tokens, sorted by probability, so a
-// node's children are visited in rank order: each tree node u keeps one frontier
-// entry, "u's next unselected child", whose key is score(u) + logq[depth(u)][cursor(u)].
-// Popping the best entry selects that child c; then u's entry moves to its next
-// child and c gets an entry for its first child.  Every pop therefore touches two
-// entries, and the frontier never holds more than one entry per selected node.
+// One wavefront per sequence.  The candidates form a K-ary tree whose depth-i
+// children are position i's top-K tokens, sorted by probability.  Every selected
+// node u (the root included) owns a stream: its not-yet-selected children in rank
+// order, scoring score(u) + logq[depth(u)][r] for r = cursor(u) .. K-1, a
+// non-increasing sequence.  A candidate outside the streams descends from a stream
+// candidate y and scores at most score(y) + logq[depth(y)][0].  So with
+//     tau = max over streams u of  head(u) + logq[depth(u) + 1][0]
+// (head(u) = u's best remaining child), every stream candidate scoring above tau
+// ranks ahead of every candidate not yet in a stream, and one round selects all of
+// them at once: they are the next pops of a best-first heap, as a set.  If that is
+// more than the remaining budget R, the round keeps the R best of them (a radix
+// select over the fp64 scores); if it is none (probability-1 positions), it takes
+// the single best stream head.  Flat drafts finish in two or three rounds; a
+// confident chain takes about one round per depth.
 //
-// Entries live in registers: node u at lane u % 64, slot u / 64.  Each lane caches
-// its best slot; a pop is one DPP max-reduction plus two exec-masked updates.  The
-// top-K log-probabilities sit in registers too (depth row = register, rank = lane),
-// so a pop reads them with v_readlane instead of an LDS round trip.
-// Scores are summed in fp64; the comparison key is the fp32 rounding of that sum
-// (rounding is monotone, so a child's key never exceeds its parent's and the popped
-// set stays prefix-closed).
-//
-// After B pops the selected nodes are renumbered canonically: by depth, then parent's
-// canonical index, then sibling rank (children of a node are selected in rank order,
-// so its selected children are exactly ranks 0..cursor-1).
+// Selection is by the fp64 score (sum of the fp32 log-probabilities along the
+// path); equal scores at the budget boundary are taken in node order.
+// The selected nodes are then renumbered canonically: by depth, then the parent's
+// canonical index, then sibling rank (a stream is consumed from its head, so a
+// node's selected children are exactly ranks 0 .. cursor-1).
 #include <limits.h>
 
 #include "ddt_internal.h"
@@ -30,18 +31,55 @@ namespace ddt {
 namespace {
 
 struct TreeSmem {
+  double* score;  // [N] node -> prefix log-probability
   float* lq;      // [L*K]
   int* ltok;      // [L*K]
-  int* parent;    // [N] node (pop order) -> parent node
+  int* hist;      // [256] radix-select histogram
+  int* parent;    // [N] node (selection order) -> parent node
   int* rank;      // [N]
   int* depth;     // [N]
   int* nkids;     // [N] selected children
-  double* score;  // [N]
   int* canon;     // [N] node -> canonical index
   int* order;     // [N] canonical index -> node
   int* first;     // [N] node -> canonical index of its first child
 };
 
+__host__ __device__ constexpr size_t tree_smem_bytes(int N, int LK) {
+  return sizeof(double) * (size_t)N + (sizeof(float) + sizeof(int)) * (size_t)LK +
+         sizeof(int) * 256 + sizeof(int) * 7 * (size_t)N;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += xchg<1>(v);
+  v += xchg<2>(v);
+  v += xchg<4>(v);
+  v += xchg<8>(v);
+  v += xchg<16>(v);
+  v += xchg<32>(v);
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, xchg<1>(v));
+  v = min(v, xchg<2>(v));
+  v = min(v, xchg<4>(v));
+  v = min(v, xchg<8>(v));
+  v = min(v, xchg<16>(v));
+  v = min(v, xchg<32>(v));
+  return v;
+}
+
+__device__ __forceinline__ double wave_max_d(double v) {
+  v = fmax(v, xchg<1>(v));
+  v = fmax(v, xchg<2>(v));
+  v = fmax(v, xchg<4>(v));
+  v = fmax(v, xchg<8>(v));
+  v = fmax(v, xchg<16>(v));
+  v = fmax(v, xchg<32>(v));
+  return v;
+}
+
+// inclusive prefix sum over lanes
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = lane_id();
 #pragma unroll
@@ -52,7 +90,13 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-template <int J, int LM>
+// order-preserving map of an fp64 score to uint64 (larger score -> larger key)
+__device__ __forceinline__ unsigned long long key_of(double x) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, x);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+template <int J>
 __global__ void __launch_bounds__(kWave)
 build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict__ topk_logq,
                   const int32_t* __restrict__ bonus, int L, int K, int B,
@@ -74,6 +118,8 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
     p += sizeof(float) * LK;
     sm.ltok = reinterpret_cast<int*>(p);
     p += sizeof(int) * LK;
+    sm.hist = reinterpret_cast<int*>(p);
+    p += sizeof(int) * 256;
     int* ip = reinterpret_cast<int*>(p);
     sm.parent = ip;
     sm.rank = ip + N;
@@ -83,93 +129,199 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
     sm.order = ip + 5 * N;
     sm.first = ip + 6 * N;
   }
-  const float* lq_g = topk_logq + (int64_t)s * LK;
-  const int32_t* tok_g = topk_tok + (int64_t)s * LK;
-  // logq table in registers: ltab[d] holds depth-row d, rank = lane (K <= 64)
-  float ltab[LM];
-#pragma unroll
-  for (int d = 0; d < LM; ++d) ltab[d] = (d < L && lane < K) ? lq_g[d * K + lane] : -INFINITY;
-  for (int i = lane; i < LK; i += kWave) sm.ltok[i] = tok_g[i];
-  for (int i = lane; i < N; i += kWave) sm.nkids[i] = 0;
+  {
+    const float* lq_g = topk_logq + (int64_t)s * LK;
+    const int32_t* tok_g = topk_tok + (int64_t)s * LK;
+    for (int i = lane; i < LK; i += kWave) {
+      sm.lq[i] = lq_g[i];
+      sm.ltok[i] = tok_g[i];
+    }
+  }
+  __syncthreads();
+  auto lq = [&](int d, int r) -> double { return (double)sm.lq[d * K + r]; };
+  // bound on the children of a depth-(d) candidate: logq[d][0], none past depth L
+  auto best_child = [&](int d) -> double { return d < L ? lq(d, 0) : -INFINITY; };
 
-  // frontier entries, node u at (lane u % 64, slot u / 64)
-  float key[J];
-  double ex[J];     // exact key: score(u) + logq[depth(u)][cursor(u)]
-  double sc[J];     // score(u)
-  int meta[J];      // depth(u) | cursor(u) << 8; cursor = rank of u's next child
+  // stream of node u at (lane u % 64, slot u / 64)
+  double sc[J];    // score(u)
+  double head[J];  // score of u's next child, -inf once the stream is closed
+  double nxt[J];   // best_child(depth(u) + 1)
+  int dep[J];      // depth(u)
+  int cur[J];      // rank of u's next child; K when closed
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    key[j] = -INFINITY;
-    ex[j] = 0.0;
     sc[j] = 0.0;
-    meta[j] = 0;
+    head[j] = -INFINITY;
+    nxt[j] = -INFINITY;
+    dep[j] = 0;
+    cur[j] = K;
   }
-  {
-    const float r0 = readlane(ltab[0], 0);
-    if (lane == 0) {  // the root's first child
-      ex[0] = (double)r0;
-      key[0] = r0;
-    }
+  if (lane == 0) {  // the root
+    cur[0] = 0;
+    head[0] = lq(0, 0);
+    nxt[0] = best_child(1);
   }
-  float bkey = key[0];
-  int bslot = 0;
 
-  int n = 1;  // nodes so far (root included)
-  for (int t = 0; t < B; ++t) {
-    const float M = wave_max(bkey);
-    if (M == -INFINITY) break;  // candidate tree exhausted
-    const int w = __ffsll((long long)ballot(bkey == M)) - 1;
-    const int j = J == 1 ? 0 : __builtin_amdgcn_readfirstlane(readlane(bslot, w));
-    const double ex_u = readlane_f64(ex[j], w);
-    const double sc_u = readlane_f64(sc[j], w);
-    const int meta_u = __builtin_amdgcn_readfirstlane(readlane(meta[j], w));
-    const int dep_u = meta_u & 0xff;
-    const int nc = (meta_u >> 8) + 1;  // u's next child rank
-    const int c = n++;                 // the selected child
-    const int dep_c = dep_u + 1;
-    const float l_sib = nc < K ? readlane(ltab[dep_u], nc) : -INFINITY;
-    const float l_kid = dep_c < L ? readlane(ltab[dep_c < LM ? dep_c : 0], 0) : -INFINITY;
-    if (lane == 0) {
-      sm.parent[c] = j * kWave + w;
-      sm.rank[c] = nc - 1;
-      sm.depth[c] = dep_c;
-      sm.score[c] = ex_u;
+  // candidates of stream j scoring above th: a prefix of the stream, found by bisection
+  auto above = [&](int j, double th) -> int {
+    if (cur[j] >= K) return 0;
+    int lo = cur[j], hi = K;  // first rank at or below th lies in [lo, hi]
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sc[j] + lq(dep[j], mid) > th)
+        lo = mid + 1;
+      else
+        hi = mid;
     }
-    // u moves on to its next child
-    if (lane == w) {
-      const double e = sc_u + (double)l_sib;
-      meta[j] = dep_u | (nc << 8);
-      ex[j] = e;
-      key[j] = l_sib == -INFINITY ? -INFINITY : (float)e;
-      bkey = key[0];
-      bslot = 0;
+    return lo - cur[j];
+  };
+
+  int n = 1;  // nodes selected so far, root included
+  while (n - 1 < B) {
+    const int R = B - (n - 1);
+    bool live = false;
+    double tl = -INFINITY;
 #pragma unroll
-      for (int i = 1; i < J; ++i)
-        if (key[i] > bkey) {
-          bkey = key[i];
-          bslot = i;
-        }
+    for (int j = 0; j < J; ++j)
+      if (cur[j] < K) {
+        live = true;
+        tl = fmax(tl, head[j] + nxt[j]);
+      }
+    if (!ballot(live)) break;  // the candidate tree is exhausted
+    const double tau = wave_max_d(tl);
+    int cnt[J];
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      cnt[j] = above(j, tau);
+      mine += cnt[j];
     }
-    // c starts at its first child
-    const int jc = c / kWave;
-    if (lane == c % kWave && jc < J) {
-      const double e = ex_u + (double)l_kid;
-      const float kk = l_kid == -INFINITY ? -INFINITY : (float)e;
-      ex[jc] = e;
-      sc[jc] = ex_u;
-      meta[jc] = dep_c;
-      key[jc] = kk;
-      if (kk > bkey) {
-        bkey = kk;
-        bslot = jc;
+    int total = wave_sum_i(mine);
+
+    if (total == 0) {
+      // nothing clears tau: take the single best head, the lowest node on ties
+      double hb = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (cur[j] < K) hb = fmax(hb, head[j]);
+      const double hm = wave_max_d(hb);
+      int pick = INT_MAX;
+#pragma unroll
+      for (int j = J - 1; j >= 0; --j)
+        if (cur[j] < K && head[j] == hm) pick = j * kWave + lane;
+      pick = wave_min_i(pick);
+#pragma unroll
+      for (int j = 0; j < J; ++j) cnt[j] = (j * kWave + lane == pick) ? 1 : 0;
+      total = 1;
+    } else if (total > R) {
+      // keep the R best.  Radix select over the 64-bit keys finds T, the R-th
+      // largest key, and how many keys equal to T belong in (k).
+      unsigned long long prefix = 0ull, pmask = 0ull;
+      int k = R;
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int b = lane; b < 256; b += kWave) sm.hist[b] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          for (int i = 0; i < cnt[j]; ++i) {
+            const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i));
+            if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1);
+          }
+        __syncthreads();
+        // lane l holds bins 255-4l .. 252-4l: the scan runs from the top bin down
+        int h[4], loc = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          h[q] = sm.hist[255 - 4 * lane - q];
+          loc += h[q];
+        }
+        const int incl = wave_incl_scan(loc);
+        const int excl = incl - loc;
+        const int src = max(__ffsll((long long)ballot(excl < k && incl >= k)) - 1, 0);
+        int bin = 0, higher = 0;
+        if (lane == src) {
+          int acc = excl;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (acc + h[q] >= k) {
+              bin = 255 - 4 * lane - q;
+              higher = acc;
+              break;
+            }
+            acc += h[q];
+          }
+        }
+        bin = readlane(bin, src);
+        higher = readlane(higher, src);
+        k -= higher;
+        prefix |= (unsigned long long)bin << shift;
+        pmask |= 255ull << shift;
+        __syncthreads();
+      }
+      // per stream: the keys above T, then the first k keys equal to T in node order
+      int gt[J], eq[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        gt[j] = 0;
+        eq[j] = 0;
+        for (int i = 0; i < cnt[j]; ++i) {
+          const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i));
+          gt[j] += key > prefix;
+          eq[j] += key == prefix;
+        }
+      }
+      int before = 0;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int incl = wave_incl_scan(eq[j]);
+        const int take = min(max(k - (before + incl - eq[j]), 0), eq[j]);
+        cnt[j] = gt[j] + take;
+        before += readlane(incl, kWave - 1);
+      }
+      total = R;
+    }
+
+    // the round's nodes get ids n .. n + total - 1 in (slot, lane) order
+    int base = n;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int incl = wave_incl_scan(cnt[j]);
+      const int firstid = base + incl - cnt[j];
+      const int u = j * kWave + lane;
+      for (int i = 0; i < cnt[j]; ++i) {
+        const int x = firstid + i;
+        sm.parent[x] = u;
+        sm.rank[x] = cur[j] + i;
+        sm.depth[x] = dep[j] + 1;
+        sm.score[x] = sc[j] + lq(dep[j], cur[j] + i);
+      }
+      if (cnt[j] > 0) {
+        cur[j] += cnt[j];
+        head[j] = cur[j] < K ? sc[j] + lq(dep[j], cur[j]) : -INFINITY;
+      }
+      base += readlane(incl, kWave - 1);
+    }
+    __syncthreads();
+    // each new node opens its stream
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int x = j * kWave + lane;
+      if (x >= n && x < n + total) {
+        dep[j] = sm.depth[x];
+        sc[j] = sm.score[x];
+        const bool open = dep[j] < L;
+        cur[j] = open ? 0 : K;
+        head[j] = open ? sc[j] + lq(dep[j], 0) : -INFINITY;
+        nxt[j] = best_child(dep[j] + 1);
       }
     }
+    n += total;
   }
-  // children counts of every node
+  // selected children of every node: ranks 0 .. cursor-1 of an open stream
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int u = j * kWave + lane;
-    if (u < n) sm.nkids[u] = meta[j] >> 8;
+    if (u < n) sm.nkids[u] = dep[j] < L ? cur[j] : 0;
   }
   if (lane == 0) {
     sm.parent[0] = -1;
@@ -189,9 +341,9 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
     for (int p0 = lvl_lo; p0 < lvl_hi; p0 += kWave) {
       const int p = p0 + lane;
       const int v = p < lvl_hi ? sm.order[p] : 0;
-      const int cnt = p < lvl_hi ? sm.nkids[v] : 0;
-      const int incl = wave_incl_scan(cnt);
-      if (p < lvl_hi) sm.first[v] = base + incl - cnt;
+      const int c = p < lvl_hi ? sm.nkids[v] : 0;
+      const int incl = wave_incl_scan(c);
+      if (p < lvl_hi) sm.first[v] = base + incl - c;
       base += readlane(incl, kWave - 1);
     }
     __syncthreads();
@@ -228,30 +380,19 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
   if (lane == 0) num_nodes[s] = n;
 }
 
-template <int J, int LM>
+template <int J>
 hipError_t launch_j(const int32_t* tok, const float* logq, const int32_t* bonus, int S, int L,
                     int K, int B, int32_t* tree_tok, int32_t* parent, int32_t* depth,
                     float* node_logq, int32_t* num_nodes, hipStream_t st) {
-  const int N = B + 1;
-  const size_t smem = sizeof(double) * N + (sizeof(float) + sizeof(int)) * (size_t)L * K +
-                      sizeof(int) * 7 * (size_t)N;
+  const size_t smem = tree_smem_bytes(B + 1, L * K);
   if (smem > 48 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_tree_kernel<J, LM>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_tree_kernel<J>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((build_tree_kernel<J, LM>), dim3(S), dim3(kWave), smem, st, tok, logq, bonus,
-                     L, K, B, tree_tok, parent, depth, node_logq, num_nodes);
+  hipLaunchKernelGGL((build_tree_kernel<J>), dim3(S), dim3(kWave), smem, st, tok, logq, bonus, L,
+                     K, B, tree_tok, parent, depth, node_logq, num_nodes);
   return hipGetLastError();
-}
-
-template <int J>
-hipError_t launch_l(const int32_t* tok, const float* logq, const int32_t* bonus, int S, int L,
-                    int K, int B, int32_t* tree_tok, int32_t* parent, int32_t* depth,
-                    float* node_logq, int32_t* num_nodes, hipStream_t st) {
-  if (L <= 16)
-    return launch_j<J, 16>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq, num_nodes, st);
-  return launch_j<J, 64>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq, num_nodes, st);
 }
 
 }  // namespace
@@ -260,11 +401,10 @@ hipError_t launch_build_tree(const int32_t* tok, const float* logq, const int32_
                              int L, int K, int B, int32_t* tree_tok, int32_t* parent,
                              int32_t* depth, float* node_logq, int32_t* num_nodes,
                              hipStream_t st) {
-  // frontier entries: one per node that can still get children, at most B of them
-  // are ever created (the last selected node's entry is never popped).
+  // one stream per node: B + 1 of them, 64 per register slot
   const int slots = (int)ceil_div(B + 1, kWave);
 #define DDT_J(JJ) \
-  return launch_l<JJ>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq, num_nodes, st)
+  return launch_j<JJ>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq, num_nodes, st)
   if (slots <= 1) DDT_J(1);
   if (slots <= 2) DDT_J(2);
   if (slots <= 4) DDT_J(4);

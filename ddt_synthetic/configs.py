@@ -29,6 +29,7 @@ class Config:
     D: int
     dtype: str               # "f32" or "bf16" for Q/K/V and the attention output
     near_tie: str            # "all": every candidate pair; "boundary": selection boundary
+    chain_boost: float = 0.0  # extra logit on the planted chain token (confident drafts)
 
     @property
     def N(self) -> int:

@@ -63,7 +63,7 @@ def draft(cfg: Config, seq: int, attempt: int = 0) -> Dict[str, np.ndarray]:
     logits = (np.float32(2.0) * z).astype(np.float32)
     for i in range(1, cfg.L + 1):  # position i holds c_i
         t = chain[i - 1]
-        logits[i - 1, t] = np.float32(np.float64(logits[i - 1, t]) + (6.0 - 0.4 * i))
+        logits[i - 1, t] = np.float32(np.float64(logits[i - 1, t]) + (6.0 - 0.4 * i) + cfg.chain_boost)
     return {"logits": logits, "chain": chain, "bonus": bonus}
 
 

@@ -156,6 +156,10 @@ def test_sharp_tree_keys(dtype):
     ("P0", dict(prefix=(0, 0))), ("P1", dict(prefix=(1, 1))), ("P7", dict(prefix=(7, 7))),
     ("shortfall", dict(L=2, K=3, B=20)), ("wide", dict(K=64, B=200, L=3, V=400)),
     ("deep", dict(L=64, K=2, B=150, V=40)), ("gqa8", dict(Hq=16, Hkv=2)), ("mha", dict(Hq=4, Hkv=4)),
+    # confident drafts: chain log-probabilities of exactly 0 (boost 200) or ~1e-12 (boost 30),
+    # which the tree builder meets one depth per round
+    ("sure", dict(B=12, chain_boost=200.0)), ("sure-deep", dict(L=16, K=4, B=60, V=300, chain_boost=200.0)),
+    ("near-sure", dict(L=8, B=30, chain_boost=30.0)),
 ])
 def test_edge_cases(name, kw):
     base = dict(S=2, L=4, V=257, K=4, B=12, prefix=(5, 150), Hq=8, Hkv=2, D=128, dtype="bf16")
