@@ -87,7 +87,8 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
 
 
 def _ws(nbytes: int, device) -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    # zero-filled: the completion counters at the front of a workspace start at zero
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 # ----------------------------------------------------------------------------- entry points

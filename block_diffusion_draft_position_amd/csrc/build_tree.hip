@@ -25,28 +25,36 @@
 // node's selected children are exactly ranks 0 .. cursor-1).
 #include <limits.h>
 
+#include <type_traits>
+
 #include "ddt_internal.h"
 
 namespace ddt {
 namespace {
 
+constexpr int kRankCap = 256;  // final rounds with at most this many candidates rank them exactly
+
 struct TreeSmem {
+  unsigned long long* key;  // [kRankCap] final-round candidate keys
+  int* sel;                 // [kRankCap] candidate taken?
   double* score;  // [N] node -> prefix log-probability
+  double* head;   // [N] node -> score of its first child (-inf: no children possible)
+  double* nxt;    // [N] node -> bound on its grandchildren's step, logq[depth + 1][0]
   float* lq;      // [L*K]
   int* ltok;      // [L*K]
   int* hist;      // [256] radix-select histogram
   int* parent;    // [N] node (selection order) -> parent node
-  int* rank;      // [N]
-  int* depth;     // [N]
-  int* nkids;     // [N] selected children
+  int* rank;      // [N] node -> sibling rank
+  int* depth;     // [N] node -> depth
   int* canon;     // [N] node -> canonical index
   int* order;     // [N] canonical index -> node
+  int* nkc;       // [N] canonical index -> number of selected children
   int* first;     // [N] node -> canonical index of its first child
 };
 
 __host__ __device__ constexpr size_t tree_smem_bytes(int N, int LK) {
-  return sizeof(double) * (size_t)N + (sizeof(float) + sizeof(int)) * (size_t)LK +
-         sizeof(int) * 256 + sizeof(int) * 7 * (size_t)N;
+  return (sizeof(unsigned long long) + sizeof(int)) * kRankCap + 3 * sizeof(double) * (size_t)N +
+         (sizeof(float) + sizeof(int)) * (size_t)LK + sizeof(int) * 256 + sizeof(int) * 7 * (size_t)N;
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -79,16 +87,25 @@ __device__ __forceinline__ double wave_max_d(double v) {
   return v;
 }
 
-// inclusive prefix sum over lanes
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+template <bool MAX>
+__device__ __forceinline__ unsigned long long wave_ext_u64(unsigned long long v) {
+  auto step = [&](unsigned long long o) { v = MAX ? (o > v ? o : v) : (o < v ? o : v); };
+  auto x = [&](auto tag) {
+    constexpr int S = decltype(tag)::value;
+    const int lo = xchg<S>((int)(unsigned)(v & 0xffffffffull));
+    const int hi = xchg<S>((int)(unsigned)(v >> 32));
+    return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+  };
+  step(x(std::integral_constant<int, 1>{}));
+  step(x(std::integral_constant<int, 2>{}));
+  step(x(std::integral_constant<int, 4>{}));
+  step(x(std::integral_constant<int, 8>{}));
+  step(x(std::integral_constant<int, 16>{}));
+  step(x(std::integral_constant<int, 32>{}));
   return v;
 }
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) { return wave_ext_u64<true>(v); }
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) { return wave_ext_u64<false>(v); }
 
 // order-preserving map of an fp64 score to uint64 (larger score -> larger key)
 __device__ __forceinline__ unsigned long long key_of(double x) {
@@ -112,8 +129,16 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
   TreeSmem sm;
   {
     unsigned char* p = smem_raw;
+    sm.key = reinterpret_cast<unsigned long long*>(p);
+    p += sizeof(unsigned long long) * kRankCap;
     sm.score = reinterpret_cast<double*>(p);
     p += sizeof(double) * N;
+    sm.head = reinterpret_cast<double*>(p);
+    p += sizeof(double) * N;
+    sm.nxt = reinterpret_cast<double*>(p);
+    p += sizeof(double) * N;
+    sm.sel = reinterpret_cast<int*>(p);
+    p += sizeof(int) * kRankCap;
     sm.lq = reinterpret_cast<float*>(p);
     p += sizeof(float) * LK;
     sm.ltok = reinterpret_cast<int*>(p);
@@ -124,9 +149,9 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
     sm.parent = ip;
     sm.rank = ip + N;
     sm.depth = ip + 2 * N;
-    sm.nkids = ip + 3 * N;
-    sm.canon = ip + 4 * N;
-    sm.order = ip + 5 * N;
+    sm.canon = ip + 3 * N;
+    sm.order = ip + 4 * N;
+    sm.nkc = ip + 5 * N;
     sm.first = ip + 6 * N;
   }
   {
@@ -139,15 +164,17 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
   }
   __syncthreads();
   auto lq = [&](int d, int r) -> double { return (double)sm.lq[d * K + r]; };
-  // bound on the children of a depth-(d) candidate: logq[d][0], none past depth L
+  // bound on the children of a depth-d candidate: logq[d][0], none past depth L
   auto best_child = [&](int d) -> double { return d < L ? lq(d, 0) : -INFINITY; };
 
-  // stream of node u at (lane u % 64, slot u / 64)
+  // node u lives at (lane u % 64, slot u / 64): its stream and its place in the tree
   double sc[J];    // score(u)
   double head[J];  // score of u's next child, -inf once the stream is closed
   double nxt[J];   // best_child(depth(u) + 1)
   int dep[J];      // depth(u)
   int cur[J];      // rank of u's next child; K when closed
+  int par[J];      // parent(u)
+  int rnk[J];      // sibling rank of u
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     sc[j] = 0.0;
@@ -155,6 +182,8 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
     nxt[j] = -INFINITY;
     dep[j] = 0;
     cur[j] = K;
+    par[j] = -1;
+    rnk[j] = -1;
   }
   if (lane == 0) {  // the root
     cur[0] = 0;
@@ -162,10 +191,18 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
     nxt[0] = best_child(1);
   }
 
-  // candidates of stream j scoring above th: a prefix of the stream, found by bisection
+  // candidates of stream j scoring above th: a prefix of the stream.  Small K reads
+  // the whole row at once; larger K bisects.
   auto above = [&](int j, double th) -> int {
     if (cur[j] >= K) return 0;
-    int lo = cur[j], hi = K;  // first rank at or below th lies in [lo, hi]
+    if (K <= 16) {
+      int c = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r < K && r >= cur[j]) c += sc[j] + lq(dep[j], r) > th;
+      return c;
+    }
+    int lo = cur[j], hi = K;  // the first rank at or below th lies in [lo, hi]
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (sc[j] + lq(dep[j], mid) > th)
@@ -214,88 +251,159 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
       for (int j = 0; j < J; ++j) cnt[j] = (j * kWave + lane == pick) ? 1 : 0;
       total = 1;
     } else if (total > R) {
-      // keep the R best.  Radix select over the 64-bit keys finds T, the R-th
-      // largest key, and how many keys equal to T belong in (k).
-      unsigned long long prefix = 0ull, pmask = 0ull;
-      int k = R;
-      for (int shift = 56; shift >= 0; shift -= 8) {
-        for (int b = lane; b < 256; b += kWave) sm.hist[b] = 0;
-        __syncthreads();
+      // keep the R best.  Candidates are numbered in node order: slot, lane, rank.
+      int off[J];
+      {
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int incl = wave_scan(cnt[j]);
+          off[j] = base + incl - cnt[j];
+          base += readlane(incl, kWave - 1);
+        }
+      }
+      if (total <= kRankCap) {
+        // exact ranks: larger key first, equal keys in node order
 #pragma unroll
         for (int j = 0; j < J; ++j)
-          for (int i = 0; i < cnt[j]; ++i) {
-            const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i));
-            if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1);
-          }
+          for (int i = 0; i < cnt[j]; ++i)
+            sm.key[off[j] + i] = key_of(sc[j] + lq(dep[j], cur[j] + i));
+        const int Tp = (total + 7) & ~7;
+        if (lane < Tp - total) sm.key[total + lane] = 0ull;  // below every real key
         __syncthreads();
-        // lane l holds bins 255-4l .. 252-4l: the scan runs from the top bin down
-        int h[4], loc = 0;
+        for (int i0 = 0; i0 < total; i0 += kWave) {
+          const int i = i0 + lane;
+          const unsigned long long mk = i < total ? sm.key[i] : ~0ull;
+          int r = 0;
+          for (int j0 = 0; j0 < Tp; j0 += 8) {
+            unsigned long long kj[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          h[q] = sm.hist[255 - 4 * lane - q];
-          loc += h[q];
+            for (int u = 0; u < 8; ++u) kj[u] = sm.key[j0 + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) r += kj[u] > mk || (kj[u] == mk && j0 + u < i);
+          }
+          if (i < total) sm.sel[i] = r < R;
         }
-        const int incl = wave_incl_scan(loc);
-        const int excl = incl - loc;
-        const int src = max(__ffsll((long long)ballot(excl < k && incl >= k)) - 1, 0);
-        int bin = 0, higher = 0;
-        if (lane == src) {
-          int acc = excl;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          int c = 0;
+          for (int i = 0; i < cnt[j]; ++i) c += sm.sel[off[j] + i];
+          cnt[j] = c;
+        }
+      } else {
+        // radix select over the 64-bit keys, 8 bits per pass from the first bit where
+        // the candidates differ; k counts how many keys of the current bin belong in,
+        // and the passes stop once that bin is taken whole
+        unsigned long long kmax = 0ull, kmin = ~0ull;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (cnt[j] > 0) {
+            kmax = max(kmax, key_of(sc[j] + lq(dep[j], cur[j])));
+            kmin = min(kmin, key_of(sc[j] + lq(dep[j], cur[j] + cnt[j] - 1)));
+          }
+        kmax = wave_max_u64(kmax);
+        kmin = wave_min_u64(kmin);
+        const unsigned long long diff = kmax ^ kmin;
+        const int top = diff ? 63 - __clzll((long long)diff) : -1;
+        unsigned long long pmask = top >= 63 ? 0ull : (~0ull << (top + 1));
+        unsigned long long prefix = kmax & pmask;
+        int k = R;
+        for (int hi = top; hi >= 0; hi -= 8) {
+          const int lo = max(hi - 7, 0);
+          const int nbins = 1 << (hi - lo + 1);
+          const unsigned long long dmask = (unsigned long long)(nbins - 1);
+          for (int b = lane; b < 256; b += kWave) sm.hist[b] = 0;
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < J; ++j)
+            for (int i = 0; i < cnt[j]; ++i) {
+              const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i));
+              if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> lo) & dmask], 1);
+            }
+          __syncthreads();
+          // lane l holds bins nbins-1-4l .. nbins-4-4l: the scan runs from the top bin down
+          int h[4], loc = 0;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (acc + h[q] >= k) {
-              bin = 255 - 4 * lane - q;
-              higher = acc;
-              break;
+            const int bi = nbins - 1 - 4 * lane - q;
+            h[q] = bi >= 0 ? sm.hist[bi] : 0;
+            loc += h[q];
+          }
+          const int incl = wave_scan(loc);
+          const int excl = incl - loc;
+          const int src = max(__ffsll((long long)ballot(excl < k && incl >= k)) - 1, 0);
+          int bin = 0, higher = 0, inbin = 0;
+          if (lane == src) {
+            int acc = excl;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (acc + h[q] >= k) {
+                bin = nbins - 1 - 4 * lane - q;
+                higher = acc;
+                inbin = h[q];
+                break;
+              }
+              acc += h[q];
             }
-            acc += h[q];
+          }
+          bin = readlane(bin, src);
+          higher = readlane(higher, src);
+          inbin = readlane(inbin, src);
+          k -= higher;
+          prefix |= (unsigned long long)bin << lo;
+          pmask |= dmask << lo;
+          __syncthreads();
+          if (inbin == k) break;
+        }
+        // per stream: the keys above the bin, then the first k keys in the bin in node order
+        int gt[J], eq[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          gt[j] = 0;
+          eq[j] = 0;
+          for (int i = 0; i < cnt[j]; ++i) {
+            const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i)) & pmask;
+            gt[j] += key > prefix;
+            eq[j] += key == prefix;
           }
         }
-        bin = readlane(bin, src);
-        higher = readlane(higher, src);
-        k -= higher;
-        prefix |= (unsigned long long)bin << shift;
-        pmask |= 255ull << shift;
-        __syncthreads();
-      }
-      // per stream: the keys above T, then the first k keys equal to T in node order
-      int gt[J], eq[J];
+        int before = 0;
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        gt[j] = 0;
-        eq[j] = 0;
-        for (int i = 0; i < cnt[j]; ++i) {
-          const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i));
-          gt[j] += key > prefix;
-          eq[j] += key == prefix;
+        for (int j = 0; j < J; ++j) {
+          const int incl = wave_scan(eq[j]);
+          const int take = min(max(k - (before + incl - eq[j]), 0), eq[j]);
+          cnt[j] = gt[j] + take;
+          before += readlane(incl, kWave - 1);
         }
-      }
-      int before = 0;
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int incl = wave_incl_scan(eq[j]);
-        const int take = min(max(k - (before + incl - eq[j]), 0), eq[j]);
-        cnt[j] = gt[j] + take;
-        before += readlane(incl, kWave - 1);
       }
       total = R;
     }
 
-    // the round's nodes get ids n .. n + total - 1 in (slot, lane) order
+    // the round's nodes get ids n .. n + total - 1 in (slot, lane) order; the parent
+    // writes each child's whole stream state so the child opens it in one LDS read
     int base = n;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int incl = wave_incl_scan(cnt[j]);
+      const int incl = wave_scan(cnt[j]);
       const int firstid = base + incl - cnt[j];
       const int u = j * kWave + lane;
-      for (int i = 0; i < cnt[j]; ++i) {
-        const int x = firstid + i;
-        sm.parent[x] = u;
-        sm.rank[x] = cur[j] + i;
-        sm.depth[x] = dep[j] + 1;
-        sm.score[x] = sc[j] + lq(dep[j], cur[j] + i);
-      }
       if (cnt[j] > 0) {
+        const bool kids_open = dep[j] + 1 < L;  // may the children have children?
+        const double nn2 = best_child(dep[j] + 2);
+#pragma unroll 4
+        for (int i = 0; i < cnt[j]; ++i) {
+          const int x = firstid + i;
+          const double sx = sc[j] + lq(dep[j], cur[j] + i);
+          if (x < N) {
+            sm.parent[x] = u;
+            sm.rank[x] = cur[j] + i;
+            sm.depth[x] = dep[j] + 1;
+            sm.score[x] = sx;
+            sm.head[x] = kids_open ? sx + nxt[j] : -INFINITY;
+            sm.nxt[x] = nn2;
+          }
+        }
         cur[j] += cnt[j];
         head[j] = cur[j] < K ? sc[j] + lq(dep[j], cur[j]) : -INFINITY;
       }
@@ -309,50 +417,55 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
       if (x >= n && x < n + total) {
         dep[j] = sm.depth[x];
         sc[j] = sm.score[x];
-        const bool open = dep[j] < L;
-        cur[j] = open ? 0 : K;
-        head[j] = open ? sc[j] + lq(dep[j], 0) : -INFINITY;
-        nxt[j] = best_child(dep[j] + 1);
+        par[j] = sm.parent[x];
+        rnk[j] = sm.rank[x];
+        head[j] = sm.head[x];
+        nxt[j] = sm.nxt[x];
+        cur[j] = dep[j] < L ? 0 : K;
       }
     }
     n += total;
   }
-  // selected children of every node: ranks 0 .. cursor-1 of an open stream
+  // a stream is consumed from its head, so u's selected children are ranks 0 .. nk-1
+  int nk[J];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int u = j * kWave + lane;
-    if (u < n) sm.nkids[u] = dep[j] < L ? cur[j] : 0;
-  }
-  if (lane == 0) {
-    sm.parent[0] = -1;
-    sm.rank[0] = -1;
-    sm.depth[0] = 0;
-    sm.score[0] = 0.0;
-    sm.canon[0] = 0;
-    sm.order[0] = 0;
-  }
-  __syncthreads();
+  for (int j = 0; j < J; ++j) nk[j] = (j * kWave + lane < n && dep[j] < L) ? cur[j] : 0;
 
-  // canonical renumbering, one depth at a time
+  // canonical renumbering, one depth at a time.  Depth d's canonical order is known;
+  // a scan of its child counts gives each node the canonical index of its first child.
+  if (lane == 0) {
+    sm.order[0] = 0;
+    sm.nkc[0] = nk[0];
+    sm.canon[0] = 0;
+  }
+  int cn[J];  // canonical index of the lane's nodes
+#pragma unroll
+  for (int j = 0; j < J; ++j) cn[j] = (j == 0 && lane == 0) ? 0 : -1;
+  __syncthreads();
   int lvl_lo = 0, lvl_hi = 1;  // canonical range of the previous depth
   for (int d = 1; lvl_hi < n && d <= L; ++d) {
-    // exclusive scan of children counts over the previous depth, in canonical order
     int base = lvl_hi;
     for (int p0 = lvl_lo; p0 < lvl_hi; p0 += kWave) {
       const int p = p0 + lane;
-      const int v = p < lvl_hi ? sm.order[p] : 0;
-      const int c = p < lvl_hi ? sm.nkids[v] : 0;
-      const int incl = wave_incl_scan(c);
-      if (p < lvl_hi) sm.first[v] = base + incl - c;
+      const bool in = p < lvl_hi;
+      const int v = in ? sm.order[p] : 0;
+      const int c = in ? sm.nkc[p] : 0;
+      const int incl = wave_scan(c);
+      if (in) sm.first[v] = base + incl - c;
       base += readlane(incl, kWave - 1);
     }
     __syncthreads();
-    for (int x0 = 1; x0 < n; x0 += kWave) {
-      const int x = x0 + lane;
-      if (x < n && sm.depth[x] == d) {
-        const int ci = sm.first[sm.parent[x]] + sm.rank[x];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int x = j * kWave + lane;
+      if (x < n && x > 0 && dep[j] == d) {
+        const int ci = sm.first[par[j]] + rnk[j];
+        cn[j] = ci;
+        if (ci >= 0 && ci < N) {
+          sm.order[ci] = x;
+          sm.nkc[ci] = nk[j];
+        }
         sm.canon[x] = ci;
-        sm.order[ci] = x;
       }
     }
     __syncthreads();
@@ -360,21 +473,25 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
     lvl_hi = base;
   }
 
-  // write out in canonical order
+  // each node writes its own entry; lanes past n write the padding
   const int64_t o = (int64_t)s * N;
-  for (int ci = lane; ci < N; ci += kWave) {
-    if (ci < n) {
-      const int x = sm.order[ci];
-      const int d = sm.depth[x];
-      tree_tok[o + ci] = d == 0 ? bonus[s] : sm.ltok[(d - 1) * K + sm.rank[x]];
-      tree_parent[o + ci] = d == 0 ? -1 : sm.canon[sm.parent[x]];
-      tree_depth[o + ci] = d;
-      if (node_logq) node_logq[o + ci] = (float)sm.score[x];
-    } else {
-      tree_tok[o + ci] = -1;
-      tree_parent[o + ci] = -1;
-      tree_depth[o + ci] = -1;
-      if (node_logq) node_logq[o + ci] = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int x = j * kWave + lane;
+    if (x < n) {
+      const int ci = cn[j];
+      if (ci >= 0 && ci < N) {
+        const int d = dep[j];
+        tree_tok[o + ci] = d == 0 ? bonus[s] : sm.ltok[(d - 1) * K + rnk[j]];
+        tree_parent[o + ci] = d == 0 ? -1 : sm.canon[par[j]];
+        tree_depth[o + ci] = d;
+        if (node_logq) node_logq[o + ci] = (float)sc[j];
+      }
+    } else if (x < N) {
+      tree_tok[o + x] = -1;
+      tree_parent[o + x] = -1;
+      tree_depth[o + x] = -1;
+      if (node_logq) node_logq[o + x] = -INFINITY;
     }
   }
   if (lane == 0) num_nodes[s] = n;

@@ -99,7 +99,7 @@ int ddt_topk(const float* logits, int64_t rows, int64_t vocab, int64_t row_strid
     return DDT_ERR_INVALID_ARG;
   if (k < 1 || k > DDT_MAX_K || k > vocab) return DDT_ERR_INVALID_ARG;
   const TopkPlan plan = topk_plan(rows, vocab, k);
-  if ((int64_t)plan.nchunks * rows > INT32_MAX) return DDT_ERR_UNSUPPORTED;
+  if (rows * plan.nchunks > INT32_MAX) return DDT_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < plan.ws_bytes) return DDT_ERR_WORKSPACE;
   return hip_status(launch_topk(logits, rows, vocab, row_stride, k, out_tok, out_logq, ws, plan,
                                 as_stream(stream)));
@@ -180,7 +180,6 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
   if (S < 1 || L < 1 || L > DDT_MAX_L || B < 0 || B > DDT_MAX_B || vocab < 1 || vocab > INT32_MAX)
     return DDT_ERR_INVALID_ARG;
   const WalkPlan plan = walk_plan(S, B, vocab);
-  if ((int64_t)S * (B + 1) * plan.nchunks > INT32_MAX) return DDT_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < plan.ws_bytes) return DDT_ERR_WORKSPACE;
   return hip_status(launch_tree_walk(tree_tok, parent, num_nodes, target_logits, S, B, L, vocab,
                                      accept_len, acc_nodes, acc_tok, bonus_out, ws, plan,

@@ -96,6 +96,19 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// Inclusive prefix sum over the wave, lane 0 first: shifts within each 16-lane row,
+// then the row broadcasts carry row totals forward (lane 15 into rows 1 and 3, lane
+// 31 into rows 2 and 3).  Lanes a DPP source does not reach add the 0 they start from.
+__device__ __forceinline__ int wave_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // (value, id) pairs under `better`
 template <int S>
 __device__ __forceinline__ void argmax_step(float& v, int& i) {
@@ -116,31 +129,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   argmax_step<32>(v, i);
 }
 
-// Lane l receives lane l-1's value; lane 0 receives `first`.
-__device__ __forceinline__ int shift_up1(int v, int first) { return dpp<0x138>(v, first); }
-__device__ __forceinline__ float shift_up1(float v, float first) {
-  return __builtin_bit_cast(float, dpp<0x138>(__builtin_bit_cast(int, v), __builtin_bit_cast(int, first)));
-}
-
-// Bitonic sort of one (value, id) pair per lane into `better` order (lane 0 best).
-__device__ __forceinline__ void wave_sort(float& v, int& id) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j >= 1; j >>= 1) {
-      const float pv = __shfl_xor(v, j);
-      const int pi = __shfl_xor(id, j);
-      const bool here = ((lane & j) == 0) == ((lane & k) == 0);  // keep the better one here
-      const bool take = here ? better(pv, pi, v, id) : better(v, id, pv, pi);
-      if (take) {
-        v = pv;
-        id = pi;
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- device properties
 int cu_count();  // compute units of the current device (cached per device)
 
@@ -150,8 +138,9 @@ int cu_count();  // compute units of the current device (cached per device)
 
 // top-K
 struct TopkPlan {
-  int nchunks;
-  int64_t chunk_len;
+  int e;        // logits per lane: a wave's chunk is 64 * e
+  int nchunks;  // chunks per row
+  int merge_e;  // keys per lane per merge batch
   size_t ws_bytes;
 };
 TopkPlan topk_plan(int64_t rows, int64_t vocab, int k);
@@ -188,9 +177,10 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
 
 // walk
 struct WalkPlan {
-  int nchunks;
-  int64_t chunk_len;
-  size_t ws_bytes;
+  int waves;             // waves per workgroup (one workgroup per node row)
+  int nbatch;            // batches of waves * 64 * 32 logits per row
+  size_t counter_bytes;  // per-sequence completion counters at the front of the workspace
+  size_t ws_bytes;       // counters + one 64-bit arg-max key per node
 };
 WalkPlan walk_plan(int S, int B, int64_t vocab);
 hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,

@@ -2,12 +2,16 @@
 // the target's decoding rule from the root, accept while its token matches a child,
 // carry the first mismatch as the next bonus token).
 //
-//   argmax_partial  grid (rows x chunks), 256 threads: argmax of one chunk of one
-//                   node's target logits (larger value first, equal values by
-//                   smaller id), 16-byte streaming loads.  Rows of padding nodes
-//                   are skipped.
-//   walk_kernel     one wave per sequence: merges the chunk results into the
-//                   target's token at every node, then walks the tree.
+// One kernel.  A workgroup of up to 16 waves takes one node's row of target logits,
+// read in batches of 16-byte loads issued together, and finds its arg-max: larger
+// value first, equal values by smaller id.  The winner is stored as the node's
+// 64-bit key in the workspace (the order-preserving image of the value above the
+// complement of the id).  Padding nodes (past num_nodes) are skipped.  Each
+// workgroup then bumps its sequence's counter; the one that completes the sequence
+// reads the node keys, clears the counter for the next call, and walks the tree
+// with one wave.  Keys and counters pass between workgroups through device-scope
+// atomics only: the key store is a returning exchange, whose result is awaited
+// before the counter increment, so no cache-wide fence is needed.
 #include <limits.h>
 
 #include "ddt_internal.h"
@@ -15,85 +19,109 @@
 namespace ddt {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kMaxWaves = 16;  // waves per workgroup
+constexpr int kE = 32;         // logits per lane per batch
 
-struct ArgMax {
-  float v;
-  int i;
-};
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void take(ArgMax& a, float v, int i) {
-  if (better(v, i, a.v, a.i)) {
-    a.v = v;
-    a.i = i;
-  }
+// order-preserving map of a float to uint32
+__device__ __forceinline__ unsigned fkey(float v) {
+  const unsigned b = __builtin_bit_cast(unsigned, v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__global__ void __launch_bounds__(kThreads)
-argmax_partial(const float* __restrict__ target, const int32_t* __restrict__ num_nodes, int N,
-               int vocab, int nchunks, int64_t chunk_len, bool vec_ok,
-               ArgMax* __restrict__ part) {
-  __shared__ ArgMax red[kThreads / kWave];
-  const int64_t rowc = blockIdx.x;
-  const int c = (int)(rowc % nchunks);
-  const int64_t row = rowc / nchunks;  // s * N + n
+// (value, id) -> key: larger value wins, then smaller id.  0 means "none".
+__device__ __forceinline__ unsigned long long pack(float v, int id) {
+  return ((unsigned long long)fkey(v) << 32) | (unsigned)(0xffffffffu - (unsigned)id);
+}
+
+__device__ __forceinline__ int unpack_id(unsigned long long key) {
+  return (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
+}
+
+__global__ void __launch_bounds__(kMaxWaves * kWave)
+tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ parent,
+                 const int32_t* __restrict__ num_nodes, const float* __restrict__ target, int N,
+                 int L, int vocab, int nbatch, bool vec_ok, unsigned long long* __restrict__ best,
+                 unsigned* __restrict__ counters, int32_t* __restrict__ accept_len,
+                 int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
+                 int32_t* __restrict__ bonus_out) {
+  __shared__ unsigned long long red[kMaxWaves];
+  __shared__ int last;
+  extern __shared__ int smem[];
+  const int64_t row = blockIdx.x;  // s * N + n
   const int s = (int)(row / N);
   const int n = (int)(row % N);
-  if (n >= num_nodes[s]) return;
-  const float* x = target + row * (int64_t)vocab;
-  const int lo = (int)(c * chunk_len);
-  const int hi = (int)min<int64_t>((int64_t)lo + chunk_len, vocab);
+  const int nn = num_nodes[s];
+  if (n >= nn) return;
+  const int nw = blockDim.x / kWave;
   const int tid = threadIdx.x;
-  ArgMax a{-INFINITY, INT_MAX};
-  for (int base = lo + tid * 4; base < hi; base += kThreads * 4) {
-    if (vec_ok && base + 3 < hi) {
-      const float4 v = *reinterpret_cast<const float4*>(x + base);
-      take(a, v.x, base);
-      take(a, v.y, base + 1);
-      take(a, v.z, base + 2);
-      take(a, v.w, base + 3);
-    } else {
-      for (int j = 0; j < 4 && base + j < hi; ++j) take(a, x[base + j], base + j);
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const float* x = target + row * (int64_t)vocab;
+
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int bt = 0; bt < nbatch; ++bt) {
+    const int lo = (bt * nw + wave) * kWave * kE;
+    float v[kE];
+#pragma unroll
+    for (int b = 0; b < kE / 4; ++b) {
+      const int base = lo + (b * kWave + lane) * 4;
+      if (vec_ok && base + 3 < vocab) {
+        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + base));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[4 * b + q] = t[q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[4 * b + q] = base + q < vocab ? x[base + q] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int i = lo + ((e / 4) * kWave + lane) * 4 + e % 4;
+      if (i < vocab && better(v[e], i, bv, bi)) {
+        bv = v[e];
+        bi = i;
+      }
     }
   }
-  wave_argmax(a.v, a.i);
-  if (tid % kWave == 0) red[tid / kWave] = a;
+  wave_argmax(bv, bi);
+  if (lane == 0) red[wave] = bi == INT_MAX ? 0ull : pack(bv, bi);
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kThreads / kWave; ++w) take(a, red[w].v, red[w].i);
-    part[rowc] = a;
-  }
-}
-
-__global__ void __launch_bounds__(kWave)
-walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ parent,
-            const int32_t* __restrict__ num_nodes, const ArgMax* __restrict__ part, int N, int L,
-            int nchunks, int32_t* __restrict__ accept_len, int32_t* __restrict__ acc_nodes,
-            int32_t* __restrict__ acc_tok, int32_t* __restrict__ bonus_out) {
-  extern __shared__ int smem[];
-  int* want = smem;          // [N] target's greedy token at each node
-  int* tok = smem + N;       // [N]
-  int* par = smem + 2 * N;   // [N]
-  const int s = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int nn = num_nodes[s];
-  for (int n = lane; n < nn; n += kWave) {
-    tok[n] = tree_tok[(int64_t)s * N + n];
-    par[n] = parent[(int64_t)s * N + n];
-    const ArgMax* p = part + ((int64_t)s * N + n) * nchunks;
-    ArgMax a = p[0];
-    for (int c = 1; c < nchunks; ++c) take(a, p[c].v, p[c].i);
-    want[n] = a.i;
+    unsigned long long k = red[0];
+    for (int w = 1; w < nw; ++w) k = red[w] > k ? red[w] : k;
+    const unsigned long long old = atomicExch(&best[row], k);
+    asm volatile("" ::"v"((unsigned)old) : "memory");  // the exchange has been performed
+    const unsigned prev = atomicAdd(&counters[s], 1u);
+    last = prev == (unsigned)nn - 1u;
   }
   __syncthreads();
+  if (!last) return;
+
+  // the sequence's last workgroup: collect the target's token at every node, walk
+  int* want = smem;         // [N] target's greedy token at each node
+  int* tok = smem + N;      // [N]
+  int* par = smem + 2 * N;  // [N]
+  for (int i = tid; i < nn; i += blockDim.x) {
+    const unsigned long long k =
+        __hip_atomic_load(best + (int64_t)s * N + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    want[i] = unpack_id(k);
+    tok[i] = tree_tok[(int64_t)s * N + i];
+    par[i] = parent[(int64_t)s * N + i];
+  }
+  if (tid == 0) __hip_atomic_store(&counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tid >= kWave) return;
   int cur = 0;
   int a = 0;
   while (a < L) {
     const int wt = want[cur];
     int found = -1;
     for (int x0 = 0; x0 < nn && found < 0; x0 += kWave) {
-      const int x = x0 + lane;
-      const bool hit = x < nn && par[x] == cur && tok[x] == wt;
+      const int xi = x0 + lane;
+      const bool hit = xi < nn && par[xi] == cur && tok[xi] == wt;
       const unsigned long long m = ballot(hit);
       if (m) found = x0 + __ffsll((long long)m) - 1;
     }
@@ -120,14 +148,10 @@ walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ pa
 WalkPlan walk_plan(int S, int B, int64_t vocab) {
   WalkPlan p;
   const int64_t rows = (int64_t)S * (B + 1);
-  const int64_t target_blocks = 2048;
-  const int64_t max_chunks = std::max<int64_t>(1, vocab / 4096);
-  int64_t nch = std::min<int64_t>(std::max<int64_t>(1, ceil_div(target_blocks, rows)), max_chunks);
-  const int64_t len = (int64_t)align_up((size_t)ceil_div(vocab, nch), 4);
-  nch = ceil_div(vocab, len);
-  p.nchunks = (int)nch;
-  p.chunk_len = len;
-  p.ws_bytes = align_up((size_t)rows * nch * sizeof(ArgMax), 256);
+  p.waves = (int)std::min<int64_t>(kMaxWaves, ceil_div(vocab, (int64_t)kWave * kE));
+  p.nbatch = (int)ceil_div(vocab, (int64_t)p.waves * kWave * kE);
+  p.counter_bytes = align_up((size_t)S * sizeof(unsigned), 256);
+  p.ws_bytes = p.counter_bytes + align_up((size_t)rows * sizeof(unsigned long long), 256);
   return p;
 }
 
@@ -137,16 +161,14 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             int32_t* acc_tok, int32_t* bonus_out, void* ws, const WalkPlan& plan,
                             hipStream_t st) {
   const int N = B + 1;
-  ArgMax* part = static_cast<ArgMax*>(ws);
+  unsigned* counters = static_cast<unsigned*>(ws);
+  unsigned long long* best =
+      reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + plan.counter_bytes);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0);
-  const int64_t blocks = (int64_t)S * N * plan.nchunks;
-  hipLaunchKernelGGL(argmax_partial, dim3((unsigned)blocks), dim3(kThreads), 0, st, target,
-                     num_nodes, N, (int)vocab, plan.nchunks, plan.chunk_len, vec_ok, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(walk_kernel, dim3(S), dim3(kWave), 3 * sizeof(int) * N, st, tree_tok, parent,
-                     num_nodes, part, N, L, plan.nchunks, accept_len, acc_nodes, acc_tok,
-                     bonus_out);
+  hipLaunchKernelGGL(tree_walk_kernel, dim3((unsigned)((int64_t)S * N)), dim3(plan.waves * kWave),
+                     3 * sizeof(int) * N, st, tree_tok, parent, num_nodes, target, N, L,
+                     (int)vocab, plan.nbatch, vec_ok, best, counters, accept_len, acc_nodes,
+                     acc_tok, bonus_out);
   return hipGetLastError();
 }
 

@@ -79,9 +79,10 @@ const char* ddt_status_string(int status);
  *            equal logits in increasing token id.
  * out_logq   [rows, k] fp32: log q(token) = logit - logsumexp(row), the
  *            full-vocabulary log-softmax at temperature 1 (not renormalised over
- *            the k kept tokens).  The log-sum-exp is accumulated in fp64.
+ *            the k kept tokens).  Sums of exp are formed in fp32 over at most 32
+ *            logits per lane and in fp64 beyond that.
  * ws         device workspace of at least ddt_topk_workspace_size(rows, vocab, k)
- *            bytes (no alignment beyond 256 B needed, contents ignored).
+ *            bytes (per-chunk lists and statistics; contents ignored).
  * Errors: null pointer; rows < 1; vocab < 1 or > INT32_MAX; row_stride < vocab;
  *         k out of range; ws_bytes too small.
  */
