@@ -645,6 +645,8 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 }
 
 // Merge the splits of each row: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// Splits are visited in batches of 8 whose loads are all issued before any is used,
+// so a row costs two memory latencies per 8 splits rather than one per split.
 template <typename OutT, int D>
 __global__ void __launch_bounds__(256)
 attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
@@ -653,6 +655,7 @@ attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
              bool has_cache, OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int TPR = D / 4;            // threads per row, 4 outputs each
   constexpr int RPB = 256 / TPR;        // rows per block
+  constexpr int kB = 8;                 // splits per batch
   const int64_t rid = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int dq = (threadIdx.x % TPR) * 4;
   if (rid >= (int64_t)S * N * Hq) return;
@@ -671,21 +674,39 @@ attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
   const int64_t P = has_cache ? cu_prefix[s + 1] - cu_prefix[s] : 0;
   const int nvalid = P > 0 ? (int)min<int64_t>(nsplit, (P + chunk - 1) / chunk) : 0;
   const int64_t base = ((int64_t)s * Hkv + g) * (nsplit + 1);
-  float M = mlpart[(base + nsplit) * rows_pad + row].x;
-  for (int c = 0; c < nvalid; ++c) M = fmaxf(M, mlpart[(base + c) * rows_pad + row].x);
+  // the splits that hold keys: prefix splits 0 .. nvalid-1, then the tree split
+  const int nused = nvalid + 1;
+  auto split_of = [&](int i) { return i < nvalid ? i : nsplit; };
+  float M = -INFINITY;
+  for (int i0 = 0; i0 < nused; i0 += kB) {
+    float m[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      m[b] = i0 + b < nused ? mlpart[(base + split_of(i0 + b)) * rows_pad + row].x : -INFINITY;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) M = fmaxf(M, m[b]);
+  }
   float l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c <= nsplit; ++c) {
-    if (c < nsplit && c >= nvalid) continue;
-    const int64_t ur = (base + c) * rows_pad + row;
-    const float2 ml = mlpart[ur];
-    const float w = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-    l += w * ml.y;
-    const float4 v = *reinterpret_cast<const float4*>(opart + ur * D + dq);
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+  for (int i0 = 0; i0 < nused; i0 += kB) {
+    float2 ml[kB];
+    float4 v[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const bool ok = i0 + b < nused;
+      const int64_t ur = (base + split_of(ok ? i0 + b : 0)) * rows_pad + row;
+      ml[b] = ok ? mlpart[ur] : make_float2(-INFINITY, 0.f);
+      v[b] = ok ? *reinterpret_cast<const float4*>(opart + ur * D + dq) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const float w = (ml[b].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[b].x - M);
+      l += w * ml[b].y;
+      acc.x += w * v[b].x;
+      acc.y += w * v[b].y;
+      acc.z += w * v[b].z;
+      acc.w += w * v[b].w;
+    }
   }
   const float inv = 1.f / l;
   o[0] = (OutT)(acc.x * inv);
@@ -891,7 +912,7 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_
   const int64_t maxp = std::max<int64_t>(max_prefix, 0);
   const int64_t want = std::max<int64_t>(1, ceil_div(target, units_base));
   int64_t chunk = (int64_t)align_up((size_t)std::max<int64_t>(1, ceil_div(maxp, want)), kTile);
-  chunk = std::max<int64_t>(chunk, (D == 128 ? 4 : 2) * kTile);
+  chunk = std::max<int64_t>(chunk, kTile);
   p.chunk = chunk;
   p.nsplit = (int)std::max<int64_t>(1, ceil_div(maxp, chunk));
   const size_t rows = (size_t)S * Hkv * (p.nsplit + 1) * p.rows_pad;
