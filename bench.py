@@ -72,6 +72,37 @@ def attention_cost(cfg, prefix_lens):
     return kv + tree + q + mask, flops
 
 
+def attention_kernel(cfg):
+    if cfg.dtype != "bf16":
+        return "attn_f32"
+    return "attn_d128" if cfg.D == 128 else "attn_partial_bf16"
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_hbm_traffic.txt")
+ATTN_SOURCE = os.path.join(ROOT, "block_diffusion_draft_position_amd", "csrc", "tree_attention.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the attention main kernel, from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current kernel source."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+        with open(ATTN_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    recorded = {l[1] for l in lines if l[0] == "source_sha256"}
+    if sha not in recorded:
+        return None
+    for l in lines:
+        if l[0] == "workload" and l[1] == workload:
+            kv = dict(zip(l[2::2], l[3::2]))
+            return float(kv["traffic_bytes"])
+    return None
+
+
 def cpu_baseline(cfg, b, att, budget_s=12.0):
     """The oracle as it stands, single-threaded, on a bounded sample of the workload,
     scaled to rounds/s: steps 1-3 and the walk for one sequence, attention for a
@@ -222,11 +253,12 @@ def main():
         peak = BF16_PEAK_TFS if cfg.dtype == "bf16" else F32_PEAK_TFS
         roof = {"bound": "mfma", "achieved": flops / attn_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "attn_partial_bf16" if cfg.dtype == "bf16" else "attn_f32"
+    roof["traffic"] = measured_traffic(cfg.name)
+    roof["kernel"] = attention_kernel(cfg)
     roof["kernel_us"] = attn_s * 1e6
     roof["launches_timed"] = attn_n
-    roof["timing"] = "HIP events around each launch, eager rounds after the timed graph replays"
+    roof["timing"] = ("HIP events attached to each dispatch of the kernel (hipExtLaunchKernelGGL) "
+                      "on its stream, eager rounds right after the timed graph replays")
     roof["bytes_per_launch"] = bytes_
     roof["flops_per_launch"] = flops
     out = {

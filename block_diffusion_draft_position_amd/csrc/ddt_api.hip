@@ -42,25 +42,24 @@ Prof& prof() {
 }
 }  // namespace
 
-hipEvent_t prof_begin(hipStream_t st) {
+bool prof_events(hipEvent_t* start, hipEvent_t* stop) {
   Prof& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
-  if (!p.on) return nullptr;
+  if (!p.on) return false;
   if (p.used == p.pool.size()) {
     hipEvent_t a = nullptr, b = nullptr;
-    if (hipEventCreate(&a) != hipSuccess) return nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return false;
     if (hipEventCreate(&b) != hipSuccess) {
       (void)hipEventDestroy(a);
-      return nullptr;
+      return false;
     }
     p.pool.emplace_back(a, b);
   }
   auto& ev = p.pool[p.used++];
-  if (prof_record(ev.first, st) != hipSuccess) return nullptr;
-  return ev.second;
+  *start = ev.first;
+  *stop = ev.second;
+  return true;
 }
-
-hipError_t prof_record(hipEvent_t ev, hipStream_t st) { return hipEventRecord(ev, st); }
 
 }  // namespace ddt
 

@@ -190,10 +190,10 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             hipStream_t st);
 
 // Benchmark timing of the attention's main kernel (see ddt_attention_profiling).
-// prof_begin returns the stop event to record after the kernel, or nullptr when
-// profiling is off; it records the start event itself.
-hipEvent_t prof_begin(hipStream_t st);
-hipError_t prof_record(hipEvent_t ev, hipStream_t st);
+// While profiling is on, prof_events hands out a start/stop event pair that the
+// launch attaches to the kernel's dispatch (hipExtLaunchKernelGGL), so the pair
+// brackets the kernel's execution, not its enqueueing; otherwise it returns false.
+bool prof_events(hipEvent_t* start, hipEvent_t* stop);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -24,6 +24,7 @@
 //   Online softmax runs in base 2 with scale * log2(e) folded into one multiply.
 //
 // fp32 path: one wave per query row over all of its keys (no splits), VALU only.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "ddt_internal.h"
@@ -820,14 +821,15 @@ template <int D, int NW>
 hipError_t launch_partial(const AttnPlan& p, const void* q, const void* kc, const void* vc,
                           const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
                           const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
-                          float* opart, float2* ml, hipStream_t st) {
+                          float* opart, float2* ml, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   const int units = S * Hkv * (p.nsplit + 1);
   const int blocks = (int)(ceil_div(units, 8) * 8 * p.row_groups);
-  hipLaunchKernelGGL((attn_partial_bf16<D, NW>), dim3(blocks), dim3(NW * 64), Lds<D>::bytes, st,
-                     (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, cu,
-                     (const bf16_t*)kt, (const bf16_t*)vt, mask, nn, N, Hq, Hkv, p.G, p.R, W,
-                     p.rows_pad, p.nsplit, p.chunk, units, p.row_groups, scale * kLog2e, opart,
-                     ml);
+  hipExtLaunchKernelGGL((attn_partial_bf16<D, NW>), dim3(blocks), dim3(NW * 64), Lds<D>::bytes,
+                        st, ev0, ev1, 0, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc,
+                        cu, (const bf16_t*)kt, (const bf16_t*)vt, mask, nn, N, Hq, Hkv, p.G, p.R,
+                        W, p.rows_pad, p.nsplit, p.chunk, units, p.row_groups, scale * kLog2e,
+                        opart, ml);
   return hipGetLastError();
 }
 
@@ -835,24 +837,26 @@ template <int NW>
 hipError_t launch_d128_nw(const AttnPlan& p, const void* q, const void* kc, const void* vc,
                           const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
                           const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
-                          float* opart, float2* ml, hipStream_t st) {
+                          float* opart, float2* ml, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   const int units = S * Hkv * (p.nsplit + 1);
   const int blocks = (int)(ceil_div(units, 8) * 8 * p.row_groups);
-  hipLaunchKernelGGL((attn_d128<NW>), dim3(blocks), dim3(NW * 64), 0, st, (const bf16_t*)q,
-                     (const bf16_t*)kc, (const bf16_t*)vc, cu, (const bf16_t*)kt, (const bf16_t*)vt,
-                     mask, nn, N, Hq, Hkv, p.G, p.R, W, p.rows_pad, p.nsplit, p.chunk, units,
-                     p.row_groups, scale * kLog2e, opart, ml);
+  hipExtLaunchKernelGGL((attn_d128<NW>), dim3(blocks), dim3(NW * 64), 0, st, ev0, ev1, 0,
+                        (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, cu,
+                        (const bf16_t*)kt, (const bf16_t*)vt, mask, nn, N, Hq, Hkv, p.G, p.R, W,
+                        p.rows_pad, p.nsplit, p.chunk, units, p.row_groups, scale * kLog2e, opart,
+                        ml);
   return hipGetLastError();
 }
 
 hipError_t launch_d128(const AttnPlan& p, const void* q, const void* kc, const void* vc,
                        const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
                        const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
-                       float* opart, float2* ml, hipStream_t st) {
+                       float* opart, float2* ml, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
 #define DDT_NW(X)                                                                            \
   case X:                                                                                    \
     return launch_d128_nw<X>(p, q, kc, vc, cu, kt, vt, mask, nn, S, N, Hq, Hkv, W, scale,   \
-                             opart, ml, st);
+                             opart, ml, st, ev0, ev1);
   switch (p.waves) {
     DDT_NW(1) DDT_NW(2) DDT_NW(3) DDT_NW(4) DDT_NW(5) DDT_NW(6) DDT_NW(7) DDT_NW(8)
     default:
@@ -865,11 +869,12 @@ template <int D>
 hipError_t launch_partial_d(const AttnPlan& p, const void* q, const void* kc, const void* vc,
                             const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
                             const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
-                            float* opart, float2* ml, hipStream_t st) {
+                            float* opart, float2* ml, hipStream_t st, hipEvent_t ev0,
+                            hipEvent_t ev1) {
 #define DDT_NW(X)                                                                                \
   case X:                                                                                        \
     return launch_partial<D, X>(p, q, kc, vc, cu, kt, vt, mask, nn, S, N, Hq, Hkv, W, scale, \
-                                opart, ml, st);
+                                opart, ml, st, ev0, ev1);
   switch (p.waves) {
     DDT_NW(1) DDT_NW(2) DDT_NW(3) DDT_NW(4) DDT_NW(5) DDT_NW(6) DDT_NW(7) DDT_NW(8)
     default:
@@ -929,11 +934,14 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   const int W = (N + 31) / 32;
   if (p.dtype == DDT_F32) {
     const int64_t rows = (int64_t)S * N * Hq;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (!prof_events(&ev0, &ev1)) ev0 = ev1 = nullptr;
 #define DDT_F32_D(DD)                                                                          \
   case DD:                                                                                     \
-    hipLaunchKernelGGL(attn_f32<DD>, dim3((unsigned)rows), dim3(64), 0, st, (const float*)q,   \
-                       (const float*)kc, (const float*)vc, cu_prefix, (const float*)kt,        \
-                       (const float*)vt, mask, num_nodes, N, Hq, Hkv, W, scale, (float*)out, lse); \
+    hipExtLaunchKernelGGL(attn_f32<DD>, dim3((unsigned)rows), dim3(64), 0, st, ev0, ev1, 0,    \
+                          (const float*)q, (const float*)kc, (const float*)vc, cu_prefix,      \
+                          (const float*)kt, (const float*)vt, mask, num_nodes, N, Hq, Hkv, W,  \
+                          scale, (float*)out, lse);                                            \
     return hipGetLastError();
     switch (D) {
       DDT_F32_D(32) DDT_F32_D(64) DDT_F32_D(128)
@@ -946,18 +954,15 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   float* opart = static_cast<float*>(ws);
   float2* ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up(rows * D * sizeof(float), 256));
   hipError_t e;
-  const hipEvent_t stop = prof_begin(st);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (!prof_events(&ev0, &ev1)) ev0 = ev1 = nullptr;
   switch (D) {
-    case 32: e = launch_partial_d<32>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st); break;
-    case 64: e = launch_partial_d<64>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st); break;
-    case 128: e = launch_d128(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st); break;
+    case 32: e = launch_partial_d<32>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
+    case 64: e = launch_partial_d<64>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
+    case 128: e = launch_d128(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  if (stop) {
-    e = prof_record(stop, st);
-    if (e != hipSuccess) return e;
-  }
   const int64_t total = (int64_t)S * N * Hq;
   const int rpb = 256 / (D / 4);
   const unsigned blocks = (unsigned)ceil_div(total, rpb);

@@ -201,7 +201,8 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
 /* ---------------------------------------------------------------- benchmark aid
  * Timing of the attention's main kernel (the round's dominant kernel) with HIP
  * events on the stream it runs on.  While profiling is on, every
- * ddt_tree_attention call records a start/stop event pair around that kernel.
+ * ddt_tree_attention call attaches a start/stop event pair to that kernel's
+ * dispatch (hipExtLaunchKernelGGL), so the pair brackets the kernel's execution.
  * Use it on eagerly launched calls: event pairs recorded during a HIP graph
  * capture are not readable afterwards.  ddt_attention_timing waits for the
  * recorded pairs, returns the sum of their elapsed times in milliseconds and their
