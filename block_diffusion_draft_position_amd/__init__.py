@@ -6,7 +6,7 @@ and its build script.
 """
 from ._lib import (  # noqa: F401
     DDT_BF16, DDT_F32, DDTError, EXPORTS, LIB_PATH, attention_profiling, attention_timing,
-    attention_workspace_size, ddt_build_tree,
+    attention_workspace_size, ddt_build_tree, ddt_draft_tree,
     ddt_topk, ddt_tree_attention, ddt_tree_mask, ddt_tree_walk, load,
 )
 from .round import Shape, VerifyRound  # noqa: F401

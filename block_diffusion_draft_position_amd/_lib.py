@@ -43,6 +43,9 @@ def load() -> ctypes.CDLL:
         "ddt_topk": (i32, [vp, i64, i64, i64, i32, vp, vp, vp, sz, vp]),
         "ddt_build_tree": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
         "ddt_tree_mask": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp]),
+        "ddt_draft_tree_workspace_size": (sz, [i32, i32, i64, i32]),
+        "ddt_draft_tree": (i32, [vp, i64, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, vp,
+                                 vp, vp, vp, vp, sz, vp]),
         "ddt_tree_attention_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i64]),
         "ddt_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      f32, i64, vp, vp, vp, sz, vp]),
@@ -60,7 +63,8 @@ def load() -> ctypes.CDLL:
 
 
 EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_build_tree",
-           "ddt_tree_mask", "ddt_tree_attention_workspace_size", "ddt_tree_attention",
+           "ddt_tree_mask", "ddt_draft_tree_workspace_size", "ddt_draft_tree",
+           "ddt_tree_attention_workspace_size", "ddt_tree_attention",
            "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_attention_profiling",
            "ddt_attention_timing")
 
@@ -153,6 +157,41 @@ def ddt_tree_mask(parent: torch.Tensor, depth: torch.Tensor, num_nodes: torch.Te
     _check(lib.ddt_tree_mask(_p(parent), _p(depth), _p(num_nodes), _p(cu_prefix), S, N - 1,
                              _p(mask), _p(pos_ids), _stream(dev)), "ddt_tree_mask")
     return mask, pos_ids
+
+
+def ddt_draft_tree(logits: torch.Tensor, bonus: torch.Tensor, cu_prefix: Optional[torch.Tensor],
+                   K: int, B: int, out: Optional[Dict[str, torch.Tensor]] = None, ws=None):
+    """logits [S,L,V] fp32, bonus [S], cu_prefix [S+1] or None -> dict with topk_tok,
+    topk_logq, tree_tok, parent, depth, node_logq, num_nodes, mask (int32 view of
+    uint32 bits) and pos_ids (None without cu_prefix): steps 1-3 in two launches."""
+    lib = load()
+    _dev(logits, "logits", torch.float32)
+    S, L, V = logits.shape
+    _dev(bonus, "bonus", torch.int32, (S,))
+    if cu_prefix is not None:
+        _dev(cu_prefix, "cu_prefix", torch.int64, (S + 1,))
+    dev = logits.device
+    N = B + 1
+    W = (N + 31) // 32
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = {"topk_tok": torch.empty(S, L, K, **i32),
+               "topk_logq": torch.empty(S, L, K, dtype=torch.float32, device=dev),
+               "tree_tok": torch.empty(S, N, **i32), "parent": torch.empty(S, N, **i32),
+               "depth": torch.empty(S, N, **i32),
+               "node_logq": torch.empty(S, N, dtype=torch.float32, device=dev),
+               "num_nodes": torch.empty(S, **i32), "mask": torch.empty(S, N, W, **i32),
+               "pos_ids": torch.empty(S, N, **i32) if cu_prefix is not None else None}
+    need = lib.ddt_draft_tree_workspace_size(S, L, V, K)
+    if ws is None:
+        ws = _ws(need, dev)
+    _check(lib.ddt_draft_tree(_p(logits), V, _p(bonus), _p(cu_prefix), S, L, V, K, B,
+                              _p(out.get("topk_tok")), _p(out.get("topk_logq")),
+                              _p(out["tree_tok"]), _p(out["parent"]), _p(out["depth"]),
+                              _p(out.get("node_logq")), _p(out["num_nodes"]), _p(out["mask"]),
+                              _p(out.get("pos_ids")), _p(ws), ws.numel(), _stream(dev)),
+           "ddt_draft_tree")
+    return out
 
 
 def attention_workspace_size(S, B, Hq, Hkv, D, dtype, max_prefix) -> int:

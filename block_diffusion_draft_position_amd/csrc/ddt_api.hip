@@ -126,6 +126,34 @@ int ddt_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* nu
                                      as_stream(stream)));
 }
 
+// ------------------------------------------------------------------ steps 1-3 fused
+size_t ddt_draft_tree_workspace_size(int S, int L, int64_t vocab, int K) {
+  if (S < 1 || L < 1 || vocab < 1 || K < 1 || K > DDT_MAX_K) return 0;
+  return topk_plan((int64_t)S * L, vocab, K).ws_bytes;
+}
+
+int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus,
+                   const int64_t* cu_prefix, int S, int L, int64_t vocab, int K, int B,
+                   int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
+                   int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
+                   int32_t* pos_ids, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !bonus || !tree_tok || !parent || !depth || !num_nodes || !mask)
+    return DDT_ERR_INVALID_ARG;
+  if (S < 1 || L < 1 || L > DDT_MAX_L || B < 0 || B > DDT_MAX_B || vocab < 1 ||
+      vocab > INT32_MAX || row_stride < vocab || K < 1 || K > DDT_MAX_K || K > vocab)
+    return DDT_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)S * L;
+  const TopkPlan plan = topk_plan(rows, vocab, K);
+  if (rows * plan.nchunks > INT32_MAX) return DDT_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < plan.ws_bytes) return DDT_ERR_WORKSPACE;
+  const hipStream_t st = as_stream(stream);
+  hipError_t e = launch_topk_partial(logits, rows, vocab, row_stride, K, ws, plan, st);
+  if (e != hipSuccess) return DDT_ERR_HIP;
+  return hip_status(launch_draft_tree(ws, plan, bonus, cu_prefix, S, L, K, B, topk_tok, topk_logq,
+                                      tree_tok, parent, depth, node_logq, num_nodes, mask,
+                                      cu_prefix ? pos_ids : nullptr, st));
+}
+
 // ------------------------------------------------------------------ attention
 static int attn_check(int S, int B, int Hq, int Hkv, int D, int dtype) {
   if (S < 1 || B < 0 || B > DDT_MAX_B || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)

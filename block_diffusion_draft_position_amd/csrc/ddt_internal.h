@@ -147,11 +147,25 @@ TopkPlan topk_plan(int64_t rows, int64_t vocab, int k);
 hipError_t launch_topk(const float* logits, int64_t rows, int64_t vocab, int64_t stride, int k,
                        int32_t* tok, float* logq, void* ws, const TopkPlan& plan,
                        hipStream_t st);
+// the per-chunk half of top-K: chunk lists and statistics into ws (topk_ws_parts)
+hipError_t launch_topk_partial(const float* logits, int64_t rows, int64_t vocab, int64_t stride,
+                               int k, void* ws, const TopkPlan& plan, hipStream_t st);
+void topk_ws_parts(void* ws, int64_t rows, int k, const TopkPlan& plan, unsigned long long** cand,
+                   float2** stats);
 
 // tree build
 hipError_t launch_build_tree(const int32_t* tok, const float* logq, const int32_t* bonus, int S,
                              int L, int K, int B, int32_t* tree_tok, int32_t* parent,
                              int32_t* depth, float* node_logq, int32_t* num_nodes, hipStream_t st);
+
+// top-K merge + tree + mask of every sequence in one launch, from the chunk lists
+// that launch_topk_partial left in ws
+hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t* bonus,
+                             const int64_t* cu_prefix, int S, int L, int K, int B,
+                             int32_t* topk_tok, float* topk_logq, int32_t* tree_tok,
+                             int32_t* parent, int32_t* depth, float* node_logq,
+                             int32_t* num_nodes, uint32_t* mask, int32_t* pos_ids,
+                             hipStream_t st);
 
 // mask
 hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* num_nodes,

@@ -1,0 +1,142 @@
+// The draft side of a round in one launch after the top-K chunk pass: per-position
+// top-K merge (DDTree page "策展 · X (Twitter)", section 運作流程 step 1), tree
+// selection under the node budget (核心創新; 運作流程 step 2; 理論基礎) and the
+// ancestor-only mask with position ids (核心創新; 運作流程 step 3).
+//
+// One workgroup per sequence.  Wave w merges the chunk lists of draft positions
+// w, w + NW, ... (topk::merge_row) straight into the tree builder's LDS table; wave 0
+// then selects and numbers the tree (tree::build, synchronising with wave barriers
+// while the other waves wait); finally every wave forms mask rows from the canonical
+// parent array the builder left in LDS (mask::rows).  The results are identical to
+// ddt_topk -> ddt_build_tree -> ddt_tree_mask; this path saves two launches and the
+// global round trips between them.
+#include "build_tree_device.h"
+#include "topk_device.h"
+#include "tree_mask_device.h"
+
+namespace ddt {
+namespace {
+
+// waves per workgroup: as many merge waves as registers allow next to the builder
+__host__ __device__ constexpr int waves_for(int J, int ME) {
+  return J >= 16 ? 4 : (J >= 4 || ME == 32) ? 8 : 16;
+}
+
+template <int J, bool SK, int ME>
+__global__ void __launch_bounds__(waves_for(J, ME) * kWave)
+draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __restrict__ stats,
+                  int nchunks, const int32_t* __restrict__ bonus,
+                  const int64_t* __restrict__ cu_prefix, int L, int K, int B,
+                  int32_t* __restrict__ topk_tok, float* __restrict__ topk_logq,
+                  int32_t* __restrict__ tree_tok, int32_t* __restrict__ tree_parent,
+                  int32_t* __restrict__ tree_depth, float* __restrict__ node_logq,
+                  int32_t* __restrict__ num_nodes, uint32_t* __restrict__ mask,
+                  int32_t* __restrict__ pos_ids) {
+  constexpr int NW = waves_for(J, ME);
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int nn_s;
+  const int s = blockIdx.x;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int N = B + 1;
+  const int LK = L * K;
+  const int W = (N + 31) / 32;
+  topk::WaveLds* wl = reinterpret_cast<topk::WaveLds*>(smem_raw);
+  tree::TreeSmem sm = tree::carve(smem_raw + NW * sizeof(topk::WaveLds), N, LK);
+
+  for (int i = wave; i < L; i += NW) {
+    const int64_t row = (int64_t)s * L + i;
+    float rv;
+    int ri;
+    double lse;
+    topk::merge_row<ME>(row, nchunks, K, cand, stats, wl[wave], rv, ri, lse);
+    if (lane < K) {
+      const float lqv = (float)((double)rv - lse);
+      sm.lq[i * K + lane] = lqv;
+      sm.ltok[i * K + lane] = ri;
+      if (topk_tok) topk_tok[row * K + lane] = ri;
+      if (topk_logq) topk_logq[row * K + lane] = lqv;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t o = (int64_t)s * N;
+    const int P = (pos_ids && cu_prefix) ? (int)(cu_prefix[s + 1] - cu_prefix[s]) : 0;
+    const int n = tree::build<J, SK>(sm, L, K, B, bonus[s], tree_tok + o, tree_parent + o,
+                                     tree_depth + o, node_logq ? node_logq + o : nullptr,
+                                     (pos_ids && cu_prefix) ? pos_ids + o : nullptr, P,
+                                     [] { topk::wave_lds_sync(); });
+    if (lane == 0) {
+      num_nodes[s] = n;
+      nn_s = n;
+    }
+  }
+  __syncthreads();
+  mask::rows(sm.cpar, nn_s, N, W, mask + (int64_t)s * N * W, threadIdx.x, NW * kWave);
+}
+
+template <int J, bool SK, int ME>
+hipError_t launch_jkm(const unsigned long long* cand, const float2* stats, int nchunks,
+                      const int32_t* bonus, const int64_t* cu_prefix, int S, int L, int K, int B,
+                      int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
+                      int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
+                      int32_t* pos_ids, hipStream_t st) {
+  constexpr int NW = waves_for(J, ME);
+  const size_t smem = NW * sizeof(topk::WaveLds) + tree::smem_bytes(B + 1, L * K);
+  if (smem > 48 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&draft_tree_kernel<J, SK, ME>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((draft_tree_kernel<J, SK, ME>), dim3(S), dim3(NW * kWave), smem, st, cand,
+                     stats, nchunks, bonus, cu_prefix, L, K, B, topk_tok, topk_logq, tree_tok,
+                     parent, depth, node_logq, num_nodes, mask, pos_ids);
+  return hipGetLastError();
+}
+
+template <int J, int ME>
+hipError_t launch_jm(bool sk, const unsigned long long* cand, const float2* stats, int nchunks,
+                     const int32_t* bonus, const int64_t* cu_prefix, int S, int L, int K, int B,
+                     int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
+                     int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
+                     int32_t* pos_ids, hipStream_t st) {
+  if constexpr (J <= 2) {
+    if (sk)
+      return launch_jkm<J, true, ME>(cand, stats, nchunks, bonus, cu_prefix, S, L, K, B, topk_tok,
+                                     topk_logq, tree_tok, parent, depth, node_logq, num_nodes,
+                                     mask, pos_ids, st);
+  }
+  return launch_jkm<J, false, ME>(cand, stats, nchunks, bonus, cu_prefix, S, L, K, B, topk_tok,
+                                  topk_logq, tree_tok, parent, depth, node_logq, num_nodes, mask,
+                                  pos_ids, st);
+}
+
+}  // namespace
+
+hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t* bonus,
+                             const int64_t* cu_prefix, int S, int L, int K, int B,
+                             int32_t* topk_tok, float* topk_logq, int32_t* tree_tok,
+                             int32_t* parent, int32_t* depth, float* node_logq,
+                             int32_t* num_nodes, uint32_t* mask, int32_t* pos_ids,
+                             hipStream_t st) {
+  unsigned long long* cand;
+  float2* stats;
+  topk_ws_parts(const_cast<void*>(ws), (int64_t)S * L, K, plan, &cand, &stats);
+  const int slots = (int)ceil_div(B + 1, kWave);
+  const bool sk = K <= 16;
+#define DDT_ARGS                                                                                \
+  sk, cand, stats, plan.nchunks, bonus, cu_prefix, S, L, K, B, topk_tok, topk_logq, tree_tok, \
+      parent, depth, node_logq, num_nodes, mask, pos_ids, st
+#define DDT_J(JJ)                                                              \
+  return plan.merge_e == 8 ? launch_jm<JJ, 8>(DDT_ARGS) : launch_jm<JJ, 32>(DDT_ARGS)
+  if (slots <= 1) DDT_J(1);
+  if (slots <= 2) DDT_J(2);
+  if (slots <= 4) DDT_J(4);
+  if (slots <= 8) DDT_J(8);
+  DDT_J(16);
+#undef DDT_J
+#undef DDT_ARGS
+}
+
+}  // namespace ddt

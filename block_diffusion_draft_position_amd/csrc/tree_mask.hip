@@ -2,12 +2,9 @@
 // (DDTree page "策展 · X (Twitter)": section 核心創新 for the ancestor-only mask,
 // 運作流程 step 3 for compiling the tree into the target's inputs).
 //
-// One workgroup per sequence.  The parent array is staged in LDS; a thread owns
-// one (node, mask word) item and walks parent links from the node: parents have
-// smaller indices than their children, so the walk passes the word's 32 node ids
-// in one contiguous stretch and stops below it.  Items are numbered row-major, so
-// the stores of a wave are contiguous.
-#include "ddt_internal.h"
+// One workgroup per sequence; the parent array is staged in LDS and the rows are
+// formed by mask::rows (tree_mask_device.h).
+#include "tree_mask_device.h"
 
 namespace ddt {
 namespace {
@@ -24,23 +21,7 @@ tree_mask_kernel(const int32_t* __restrict__ parent, const int32_t* __restrict__
   const int32_t* pg = parent + (int64_t)s * N;
   for (int i = threadIdx.x; i < N; i += kThreads) par[i] = pg[i];
   __syncthreads();
-  uint32_t* mrow = mask + (int64_t)s * N * W;
-  const int items = N * W;
-  for (int it = threadIdx.x; it < items; it += kThreads) {
-    const int n = it / W;
-    const int w = it % W;
-    uint32_t acc = 0u;
-    if (n < nn && (n >> 5) >= w) {
-      int x = n;
-      int guard = N;  // a malformed parent array cannot loop forever
-      while (x >= (w << 5) && guard-- > 0) {
-        if ((x >> 5) == w) acc |= 1u << (x & 31);
-        const int p = par[x];
-        x = (p < x) ? p : -1;
-      }
-    }
-    mrow[it] = acc;
-  }
+  mask::rows(par, nn, N, W, mask + (int64_t)s * N * W, threadIdx.x, kThreads);
   if (pos_ids) {
     const int32_t P = (int32_t)(cu_prefix[s + 1] - cu_prefix[s]);
     for (int n = threadIdx.x; n < N; n += kThreads)

@@ -1,8 +1,10 @@
 """One DDTree verification round on the GPU, with every buffer allocated up front.
 
-The five library calls run back to back on the current stream:
-  ddt_topk -> ddt_build_tree -> ddt_tree_mask -> ddt_tree_attention -> ddt_tree_walk
-(DDTree page "策展 · X (Twitter)", section 運作流程 steps 1-4).  The object holds
+The library calls run back to back on the current stream:
+  ddt_draft_tree (= ddt_topk -> ddt_build_tree -> ddt_tree_mask, fused)
+  -> ddt_tree_attention -> ddt_tree_walk
+(DDTree page "策展 · X (Twitter)", section 運作流程 steps 1-4); fused=False makes
+the three separate calls instead, with identical results.  The object holds
 its outputs and workspaces, so a round allocates nothing and can be captured in a
 HIP graph.  Target logits are an input here: in a real verifier they come out of
 the target model's forward over the tree, which this library does not contain.
@@ -35,8 +37,9 @@ class Shape:
 
 
 class VerifyRound:
-    def __init__(self, shape: Shape, device="cuda"):
+    def __init__(self, shape: Shape, device="cuda", fused: bool = True):
         self.shape = sh = shape
+        self.fused = fused
         dev = torch.device(device)
         self.device = dev
         S, L, K, N = sh.S, sh.L, sh.K, sh.N
@@ -64,6 +67,11 @@ class VerifyRound:
     def draft_tree(self, draft_logits, bonus, cu_prefix):
         """Steps 1-3: top-K, tree, mask and position ids."""
         sh = self.shape
+        if self.fused:
+            out = dict(topk_tok=self.topk_tok, topk_logq=self.topk_logq, mask=self.mask,
+                       pos_ids=self.pos_ids, **self.tree)
+            _lib.ddt_draft_tree(draft_logits, bonus, cu_prefix, sh.K, sh.B, out, self.ws_topk)
+            return
         _lib.ddt_topk(draft_logits, sh.K, self.topk_tok, self.topk_logq, self.ws_topk)
         _lib.ddt_build_tree(self.topk_tok, self.topk_logq, bonus, sh.B, self.tree)
         _lib.ddt_tree_mask(self.tree["parent"], self.tree["depth"], self.tree["num_nodes"],

@@ -14,6 +14,7 @@
  *
  * One round for S sequences is
  *   ddt_topk -> ddt_build_tree -> ddt_tree_mask -> ddt_tree_attention -> ddt_tree_walk
+ * and ddt_draft_tree does the first three in two launches, with identical results.
  * (the target model's layers around the attention are the caller's).
  *
  * Conventions shared by every entry point
@@ -138,6 +139,28 @@ int ddt_build_tree(const int32_t* topk_tok, const float* topk_logq, const int32_
 int ddt_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* num_nodes,
                   const int64_t* cu_prefix, int S, int B, uint32_t* mask, int32_t* pos_ids,
                   void* stream);
+
+/* ---------------------------------------------------------------- steps 1-3 fused
+ * ddt_topk, ddt_build_tree and ddt_tree_mask in two launches (a top-K pass over the
+ * vocabulary chunks, then one workgroup per sequence that merges the chunks, builds
+ * the tree and forms its mask).  Every output is bit-identical to the three calls.
+ *
+ * logits      [S, L, vocab] fp32; row (s, i) at logits + (s * L + i) * row_stride.
+ * bonus       [S]; cu_prefix nullable [S+1] (needed for pos_ids).
+ * Limits as for the three calls: 1 <= L <= DDT_MAX_L, 1 <= K <= min(vocab,
+ * DDT_MAX_K), 0 <= B <= DDT_MAX_B.
+ * topk_tok, topk_logq [S, L, K], nullable: the top-K step's outputs.
+ * tree_tok, parent, depth, node_logq (nullable), num_nodes: as ddt_build_tree.
+ * mask [S, N, W] and pos_ids (nullable; written only with cu_prefix): as ddt_tree_mask.
+ * ws          at least ddt_draft_tree_workspace_size(S, L, vocab, K) bytes.
+ * Errors: null required pointer; a size out of range; ws_bytes too small.
+ */
+size_t ddt_draft_tree_workspace_size(int S, int L, int64_t vocab, int K);
+int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus,
+                   const int64_t* cu_prefix, int S, int L, int64_t vocab, int K, int B,
+                   int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
+                   int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
+                   int32_t* pos_ids, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- step 4 (attention)
  * Grouped-query tree attention: the whole tree is scored in one target forward

@@ -68,6 +68,26 @@ def test_build_tree_validation():
     assert f(a[0], a[1], a[2], 1, 4, 4, -1, a[3], a[4], a[5], None, a[6], None) == -1
 
 
+def test_draft_tree_validation():
+    lib = ddt.load()
+    f = lib.ddt_draft_tree
+    a = [_fake(i) for i in range(1, 20)]
+
+    def call(S=1, L=4, V=64, K=4, B=8, stride=64, ws_bytes=1 << 20, logits=a[0]):
+        return f(logits, stride, a[1], a[2], S, L, V, K, B, a[3], a[4], a[5], a[6], a[7], a[8],
+                 a[9], a[10], a[11], a[12], ws_bytes, None)
+    assert call(logits=None) == -1
+    assert call(S=0) == -1
+    assert call(L=65) == -1
+    assert call(K=65) == -1
+    assert call(V=3, stride=3) == -1          # K > V
+    assert call(stride=63) == -1              # stride < V
+    assert call(B=1024) == -1
+    need = lib.ddt_draft_tree_workspace_size(1, 4, 64, 4)
+    assert need == lib.ddt_topk_workspace_size(4, 64, 4) > 0
+    assert call(ws_bytes=need - 1) == -3
+
+
 def test_mask_validation():
     f = ddt.load().ddt_tree_mask
     a = [_fake(i) for i in range(1, 10)]

@@ -34,10 +34,11 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def run_case(cfg, att=None, rows_per_seq=None, sharp=False, seed_rows=0):
-    """Full round on the GPU and in the oracle; compare everything."""
+def run_case(cfg, att=None, rows_per_seq=None, sharp=False, seed_rows=0, fused=False):
+    """Full round on the GPU and in the oracle; compare everything.  fused: steps 1-3
+    through ddt_draft_tree instead of ddt_topk, ddt_build_tree and ddt_tree_mask."""
     _say(f"[case] {cfg.name} S={cfg.S} L={cfg.L} V={cfg.V} K={cfg.K} B={cfg.B} P={cfg.prefix} "
-         f"Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} {cfg.dtype} sharp={sharp}")
+         f"Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} {cfg.dtype} sharp={sharp} fused={fused}")
     if att is None:
         att = attempts(cfg)
     b = gen.batch(cfg, att)
@@ -54,9 +55,14 @@ def run_case(cfg, att=None, rows_per_seq=None, sharp=False, seed_rows=0):
     # ---- GPU
     d = upload(b)
     d["target"] = dev_tensor(tl)
-    tok, lq = ddt.ddt_topk(d["draft_logits"], cfg.K)
-    tree = ddt.ddt_build_tree(tok, lq, d["bonus"], cfg.B)
-    mask, pos = ddt.ddt_tree_mask(tree["parent"], tree["depth"], tree["num_nodes"], d["cu_prefix"])
+    if fused:
+        dt = ddt.ddt_draft_tree(d["draft_logits"], d["bonus"], d["cu_prefix"], cfg.K, cfg.B)
+        tok, lq, mask, pos = dt["topk_tok"], dt["topk_logq"], dt["mask"], dt["pos_ids"]
+        tree = {k: dt[k] for k in ("tree_tok", "parent", "depth", "node_logq", "num_nodes")}
+    else:
+        tok, lq = ddt.ddt_topk(d["draft_logits"], cfg.K)
+        tree = ddt.ddt_build_tree(tok, lq, d["bonus"], cfg.B)
+        mask, pos = ddt.ddt_tree_mask(tree["parent"], tree["depth"], tree["num_nodes"], d["cu_prefix"])
     out, lse = ddt.ddt_tree_attention(d["q"], d["k_cache"], d["v_cache"], d["cu_prefix"], d["k_tree"],
                                       d["v_tree"], mask, tree["num_nodes"], scale)
     walk = ddt.ddt_tree_walk(tree["tree_tok"], tree["parent"], tree["num_nodes"], d["target"], cfg.L)
@@ -161,17 +167,35 @@ def test_sharp_tree_keys(dtype):
     ("sure", dict(B=12, chain_boost=200.0)), ("sure-deep", dict(L=16, K=4, B=60, V=300, chain_boost=200.0)),
     ("near-sure", dict(L=8, B=30, chain_boost=30.0)),
 ])
-def test_edge_cases(name, kw):
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
+def test_edge_cases(name, kw, fused):
     base = dict(S=2, L=4, V=257, K=4, B=12, prefix=(5, 150), Hq=8, Hkv=2, D=128, dtype="bf16")
     base.update(kw)
     cfg = configs.custom(f"edge-{name}", **base)
-    run_case(cfg)
+    run_case(cfg, fused=fused)
 
 
-def test_large_budget_multi_word_mask():
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
+def test_large_budget_multi_word_mask(fused):
     cfg = configs.custom("bigB", S=1, L=8, V=1000, K=16, B=700, prefix=(300, 300), Hq=4, Hkv=1,
                          D=64, dtype="bf16")
-    run_case(cfg)
+    run_case(cfg, fused=fused)
+
+
+def test_fused_matches_calls_bitwise():
+    """ddt_draft_tree equals ddt_topk -> ddt_build_tree -> ddt_tree_mask bit for bit,
+    including the fp32 log-probabilities, on a long-vocabulary batch."""
+    cfg = configs.custom("fused-eq", S=3, L=12, V=40000, K=8, B=90, prefix=(10, 900), Hq=8,
+                         Hkv=2, D=128, dtype="bf16")
+    b = gen.batch(cfg, attempts(cfg), with_qkv=False)
+    d = upload(b)
+    dt = ddt.ddt_draft_tree(d["draft_logits"], d["bonus"], d["cu_prefix"], cfg.K, cfg.B)
+    tok, lq = ddt.ddt_topk(d["draft_logits"], cfg.K)
+    tree = ddt.ddt_build_tree(tok, lq, d["bonus"], cfg.B)
+    mask, pos = ddt.ddt_tree_mask(tree["parent"], tree["depth"], tree["num_nodes"], d["cu_prefix"])
+    ref = dict(topk_tok=tok, topk_logq=lq, mask=mask, pos_ids=pos, **tree)
+    for k, v in ref.items():
+        assert torch.equal(dt[k], v), k
 
 
 def test_tiny_workload_many_draws():
@@ -200,5 +224,6 @@ def test_deterministic():
 # ----------------------------------------------------------------------------- full workloads
 @pytest.mark.parametrize("name,rows", [("C0", None), ("C1", 200), ("C2", 48), ("C3-B16", 64),
                                        ("C3-B128", 64), ("C3-B512", 64), ("C4", 12)])
-def test_full_workloads(name, rows):
-    run_case(configs.get(name), rows_per_seq=rows)
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
+def test_full_workloads(name, rows, fused):
+    run_case(configs.get(name), rows_per_seq=rows, fused=fused)
