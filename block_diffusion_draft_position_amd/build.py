@@ -28,13 +28,18 @@ CFLAGS = [
 ]
 
 
+# per-file flags: the attention's max reductions need no NaN quieting (scores are
+# finite or -inf), so its kernels run with the IEEE mode bit off
+EXTRA = {"tree_attention.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -382,7 +382,7 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   Unit u;
   if (!decode_block(Hkv, nsplit + 1, row_groups, units, u)) return;
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: kept in an SGPR
   const int lane = tid % 64;
   const int g4 = lane / 16;   // 16-lane group
   const int l16 = lane % 16;
@@ -412,7 +412,15 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 
   // ---- the loads of tile t into ring stage ST: 32 instructions of 1 KB (4 key rows),
   // 16 for K then 16 for V, dealt round robin to the waves.  Rows past the split
-  // (last tile) re-read the split's last row and are masked later.
+  // (last tile) re-read the split's last row and are masked later.  A lane's element
+  // offset within a full tile is fixed, so it is formed once; per tile only the
+  // (uniform) tile base changes.
+  int loff[NLOAD];
+#pragma unroll
+  for (int j = 0; j < NLOAD; ++j) {
+    const int key = 4 * (((wave + j * NW) & 31) & 15) + g4;
+    loff[j] = key * (int)kstride + (l16 ^ swz(key)) * 8;
+  }
   auto issue = [&]<int ST>(int t) {
     const int64_t t0 = lo + (int64_t)t * kTile;
     const bool full = t0 + kTile <= hi;
@@ -421,10 +429,11 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       const int i = (wave + j * NW) & 31;
       const bool isv = i >= 16;
       const bf16_t* base = (isv ? vb : kb) + t0 * kstride;
-      int key = 4 * (i & 15) + g4;
-      const int c = l16 ^ swz(key);
-      if (!full) key = min(key, (int)(hi - 1 - t0));
-      const int off = key * (int)kstride + c * 8;
+      int off = loff[j];
+      if (!full) {
+        const int key = min(4 * (i & 15) + g4, (int)(hi - 1 - t0));
+        off = key * (int)kstride + (l16 ^ swz(4 * (i & 15) + g4)) * 8;
+      }
       unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + (i & 15) * 1024;
       __builtin_amdgcn_global_load_lds((glob_void*)(base + off), (lds_void*)dst, 16, 0, 0);
     }
@@ -587,20 +596,28 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     // ---- O^T += V^T . P^T  (V^T read transposed from the row-major tile).  The two
     // key rows a lane addresses (vrow, vrow + 16, plus 32 per key half) share one
     // swizzle, so the chunk slot is (2 db) ^ vsw_hi | vsw_lo.
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    // The fragments of head-dim block db + 1 are read while block db's MFMAs run.
+    auto vread = [&](int db, bf16x8 (&a)[2]) {
       const int slot = (((2 * db) ^ vhi) | vlo) << 4;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const unsigned char* p = Vs + vb_ + kh * 32 * 256 + slot;
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * 256));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        a[kh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    bf16x8 va[2][2];
+    vread(0, va[0]);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      if (db + 1 < 8) vread(db + 1, va[(db + 1) & 1]);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qb][kh], oacc[qb][db], 0, 0, 0);
-      }
-      if (db & 1) __builtin_amdgcn_sched_barrier(0);  // at most 8 V fragments live
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db & 1][kh], pb[qb][kh], oacc[qb][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // V fragments of two blocks live at most
     }
     // sum_k P[k][q] for every query: the same contraction with V replaced by ones
     // (the sum is of the bf16 weights the numerator uses)
