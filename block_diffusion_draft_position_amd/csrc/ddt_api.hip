@@ -137,7 +137,8 @@ int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus
                    int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
                    int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
                    int32_t* pos_ids, void* ws, size_t ws_bytes, void* stream) {
-  if (!logits || !bonus || !tree_tok || !parent || !depth || !num_nodes || !mask)
+  if (!logits || !bonus || !topk_tok || !topk_logq || !tree_tok || !parent || !depth ||
+      !num_nodes || !mask)
     return DDT_ERR_INVALID_ARG;
   if (S < 1 || L < 1 || L > DDT_MAX_L || B < 0 || B > DDT_MAX_B || vocab < 1 ||
       vocab > INT32_MAX || row_stride < vocab || K < 1 || K > DDT_MAX_K || K > vocab)

@@ -152,20 +152,25 @@ hipError_t launch_topk_partial(const float* logits, int64_t rows, int64_t vocab,
                                int k, void* ws, const TopkPlan& plan, hipStream_t st);
 void topk_ws_parts(void* ws, int64_t rows, int k, const TopkPlan& plan, unsigned long long** cand,
                    float2** stats);
+// the per-row half of top-K, from the chunk lists in ws
+hipError_t launch_topk_merge(int64_t rows, int k, int32_t* tok, float* logq, void* ws,
+                             const TopkPlan& plan, hipStream_t st);
 
 // tree build
 hipError_t launch_build_tree(const int32_t* tok, const float* logq, const int32_t* bonus, int S,
                              int L, int K, int B, int32_t* tree_tok, int32_t* parent,
                              int32_t* depth, float* node_logq, int32_t* num_nodes, hipStream_t st);
 
-// top-K merge + tree + mask of every sequence in one launch, from the chunk lists
-// that launch_topk_partial left in ws
+// top-K merge + tree + mask of every sequence from the chunk lists that
+// launch_topk_partial left in ws: one launch when a workgroup can give every draft
+// position its own merge wave (draft_tree_uses_fused), else the three kernels.
 hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t* bonus,
                              const int64_t* cu_prefix, int S, int L, int K, int B,
                              int32_t* topk_tok, float* topk_logq, int32_t* tree_tok,
                              int32_t* parent, int32_t* depth, float* node_logq,
                              int32_t* num_nodes, uint32_t* mask, int32_t* pos_ids,
                              hipStream_t st);
+bool draft_tree_uses_fused(int L, int K, int B, const TopkPlan& plan);
 
 // mask
 hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* num_nodes,

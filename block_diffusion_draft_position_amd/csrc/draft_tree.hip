@@ -112,7 +112,19 @@ hipError_t launch_jm(bool sk, const unsigned long long* cand, const float2* stat
                                   pos_ids, st);
 }
 
+int slots_for(int B) { return (int)ceil_div(B + 1, kWave); }
+
+int j_for(int B) {
+  const int slots = slots_for(B);
+  return slots <= 1 ? 1 : slots <= 2 ? 2 : slots <= 4 ? 4 : slots <= 8 ? 8 : 16;
+}
+
 }  // namespace
+
+bool draft_tree_uses_fused(int L, int K, int B, const TopkPlan& plan) {
+  (void)K;
+  return waves_for(j_for(B), plan.merge_e) >= std::min(L, 16);
+}
 
 hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t* bonus,
                              const int64_t* cu_prefix, int S, int L, int K, int B,
@@ -120,10 +132,20 @@ hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t
                              int32_t* parent, int32_t* depth, float* node_logq,
                              int32_t* num_nodes, uint32_t* mask, int32_t* pos_ids,
                              hipStream_t st) {
+  if (!draft_tree_uses_fused(L, K, B, plan)) {
+    // too few merge waves fit next to this builder: merge, build and mask separately
+    hipError_t e = launch_topk_merge((int64_t)S * L, K, topk_tok, topk_logq,
+                                     const_cast<void*>(ws), plan, st);
+    if (e != hipSuccess) return e;
+    e = launch_build_tree(topk_tok, topk_logq, bonus, S, L, K, B, tree_tok, parent, depth,
+                          node_logq, num_nodes, st);
+    if (e != hipSuccess) return e;
+    return launch_tree_mask(parent, depth, num_nodes, cu_prefix, S, B, mask, pos_ids, st);
+  }
   unsigned long long* cand;
   float2* stats;
   topk_ws_parts(const_cast<void*>(ws), (int64_t)S * L, K, plan, &cand, &stats);
-  const int slots = (int)ceil_div(B + 1, kWave);
+  const int slots = slots_for(B);
   const bool sk = K <= 16;
 #define DDT_ARGS                                                                                \
   sk, cand, stats, plan.nchunks, bonus, cu_prefix, S, L, K, B, topk_tok, topk_logq, tree_tok, \

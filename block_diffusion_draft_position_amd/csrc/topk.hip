@@ -143,10 +143,8 @@ hipError_t launch_topk_partial(const float* logits, int64_t rows, int64_t vocab,
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int64_t rows, int64_t vocab, int64_t stride, int k,
-                       int32_t* tok, float* logq, void* ws, const TopkPlan& plan, hipStream_t st) {
-  hipError_t e = launch_topk_partial(logits, rows, vocab, stride, k, ws, plan, st);
-  if (e != hipSuccess) return e;
+hipError_t launch_topk_merge(int64_t rows, int k, int32_t* tok, float* logq, void* ws,
+                             const TopkPlan& plan, hipStream_t st) {
   unsigned long long* cand;
   float2* stt;
   topk_ws_parts(ws, rows, k, plan, &cand, &stt);
@@ -157,6 +155,13 @@ hipError_t launch_topk(const float* logits, int64_t rows, int64_t vocab, int64_t
     hipLaunchKernelGGL(topk_merge<32>, dim3((unsigned)rows), dim3(kWave), 0, st, plan.nchunks, k,
                        cand, stt, tok, logq);
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int64_t rows, int64_t vocab, int64_t stride, int k,
+                       int32_t* tok, float* logq, void* ws, const TopkPlan& plan, hipStream_t st) {
+  hipError_t e = launch_topk_partial(logits, rows, vocab, stride, k, ws, plan, st);
+  if (e != hipSuccess) return e;
+  return launch_topk_merge(rows, k, tok, logq, ws, plan, st);
 }
 
 }  // namespace ddt

@@ -149,7 +149,11 @@ int ddt_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* nu
  * bonus       [S]; cu_prefix nullable [S+1] (needed for pos_ids).
  * Limits as for the three calls: 1 <= L <= DDT_MAX_L, 1 <= K <= min(vocab,
  * DDT_MAX_K), 0 <= B <= DDT_MAX_B.
- * topk_tok, topk_logq [S, L, K], nullable: the top-K step's outputs.
+ * topk_tok, topk_logq [S, L, K]: the top-K step's outputs.
+ * When a workgroup cannot give every draft position its own merge wave next to the
+ * tree builder's registers (large budgets or long chunk lists), the call runs the
+ * merge, the builder and the mask as three kernels instead of one; results are the
+ * same either way.
  * tree_tok, parent, depth, node_logq (nullable), num_nodes: as ddt_build_tree.
  * mask [S, N, W] and pos_ids (nullable; written only with cu_prefix): as ddt_tree_mask.
  * ws          at least ddt_draft_tree_workspace_size(S, L, vocab, K) bytes.

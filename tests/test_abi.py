@@ -77,6 +77,8 @@ def test_draft_tree_validation():
         return f(logits, stride, a[1], a[2], S, L, V, K, B, a[3], a[4], a[5], a[6], a[7], a[8],
                  a[9], a[10], a[11], a[12], ws_bytes, None)
     assert call(logits=None) == -1
+    assert f(a[0], 64, a[1], a[2], 1, 4, 64, 4, 8, None, a[4], a[5], a[6], a[7], a[8], a[9],
+             a[10], a[11], a[12], 1 << 20, None) == -1   # top-K outputs are required
     assert call(S=0) == -1
     assert call(L=65) == -1
     assert call(K=65) == -1
