@@ -43,13 +43,14 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
   tree::TreeSmem sm = tree::carve(smem_raw, N, LK);
   const float* lq_g = topk_logq + (int64_t)s * LK;
   const int32_t* tok_g = topk_tok + (int64_t)s * LK;
+  const int bonus_tok = bonus[s];  // requested with the table, used at the end
   for (int i = lane; i < LK; i += kWave) {
     sm.lq[i] = lq_g[i];
     sm.ltok[i] = tok_g[i];
   }
   __syncthreads();
   const int64_t o = (int64_t)s * N;
-  const int n = tree::build<J, SK>(sm, L, K, B, bonus[s], tree_tok + o, tree_parent + o,
+  const int n = tree::build<J, SK>(sm, L, K, B, bonus_tok, tree_tok + o, tree_parent + o,
                                    tree_depth + o, node_logq ? node_logq + o : nullptr, nullptr,
                                    0, [] { __syncthreads(); });
   if (lane == 0) num_nodes[s] = n;

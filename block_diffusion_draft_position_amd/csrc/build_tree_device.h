@@ -246,67 +246,7 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
           base += readlane(incl, kWave - 1);
         }
       }
-      if (total <= kWave) {
-        // one candidate per lane: a bit-by-bit ballot search from the first bit where
-        // the keys differ finds the R-th largest key; it stops as soon as exactly R
-        // keys reach the prefix.  Equal keys at the boundary go in node order.
-        if constexpr (SK) {
-#pragma unroll
-          for (int j = 0; j < J; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (r >= cur[j] && r < cur[j] + cnt[j])
-                sm.key[off[j] + r - cur[j]] = key_of(sc[j] + (double)rowv[j][r]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < J; ++j)
-            for (int i = 0; i < cnt[j]; ++i)
-              sm.key[off[j] + i] = key_of(sc[j] + lq(dep[j], cur[j] + i));
-        }
-        sync();
-        const bool has = lane < total;
-        const unsigned long long mk = has ? sm.key[lane] : 0ull;  // real keys are > 0
-        const unsigned long long kmax = wave_max_u64(mk);
-        const unsigned long long kmin = wave_min_u64(has ? mk : ~0ull);
-        const unsigned long long diff = kmax ^ kmin;
-        int b = diff ? 63 - __clzll((long long)diff) : -1;
-        unsigned long long t = b >= 63 ? 0ull : (kmax & (~0ull << (b + 1)));
-        bool exact = false;
-        for (; b >= 0; --b) {
-          const unsigned long long c = t | (1ull << b);
-          const int nc = __popcll(ballot(has && mk >= c));
-          if (nc >= R) t = c;
-          if (nc == R) {
-            exact = true;
-            break;
-          }
-        }
-        bool sel;
-        if (exact) {
-          sel = has && mk >= t;
-        } else {  // t is the R-th largest key; ties at t in lane (= node) order
-          const int gt = __popcll(ballot(has && mk > t));
-          const unsigned long long eqm = ballot(has && mk == t);
-          const int before = __popcll(eqm & ((1ull << lane) - 1ull));
-          sel = has && (mk > t || (mk == t && before < R - gt));
-        }
-        if (has) sm.sel[lane] = sel;
-        sync();
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-          int c = 0;
-          if constexpr (SK) {
-            int sv[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sv[i] = i < cnt[j] ? sm.sel[off[j] + i] : 0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) c += sv[i];
-          } else {
-            for (int i = 0; i < cnt[j]; ++i) c += sm.sel[off[j] + i];
-          }
-          cnt[j] = c;
-        }
-      } else if (total <= kRankCap) {
+      if (total <= kRankCap) {
         // exact ranks: larger key first, equal keys in node order
         if constexpr (SK) {
 #pragma unroll

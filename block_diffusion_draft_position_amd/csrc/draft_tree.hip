@@ -43,6 +43,9 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
   const int W = (N + 31) / 32;
   topk::WaveLds* wl = reinterpret_cast<topk::WaveLds*>(smem_raw);
   tree::TreeSmem sm = tree::carve(smem_raw + NW * sizeof(topk::WaveLds), N, LK);
+  // the builder's scalars, requested now so they arrive during the merge
+  const int bonus_tok = bonus[s];
+  const int P = (pos_ids && cu_prefix) ? (int)(cu_prefix[s + 1] - cu_prefix[s]) : 0;
 
   for (int i = wave; i < L; i += NW) {
     const int64_t row = (int64_t)s * L + i;
@@ -61,8 +64,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
   __syncthreads();
   if (wave == 0) {
     const int64_t o = (int64_t)s * N;
-    const int P = (pos_ids && cu_prefix) ? (int)(cu_prefix[s + 1] - cu_prefix[s]) : 0;
-    const int n = tree::build<J, SK>(sm, L, K, B, bonus[s], tree_tok + o, tree_parent + o,
+    const int n = tree::build<J, SK>(sm, L, K, B, bonus_tok, tree_tok + o, tree_parent + o,
                                      tree_depth + o, node_logq ? node_logq + o : nullptr,
                                      (pos_ids && cu_prefix) ? pos_ids + o : nullptr, P,
                                      [] { topk::wave_lds_sync(); });

@@ -16,11 +16,10 @@
 //                 lanes, merges them with the same wave_topk, folds the statistics
 //                 into the log-sum-exp (fp64) and writes tokens and log-probabilities.
 //
-// wave_topk: a bit-by-bit ballot search finds t, the K-th largest of the 64 per-lane
-// maxima.  At least K lanes hold a value >= t, so every member of the top-K is >= t,
-// and usually only a few more values are (about K ln(64/(64-K)) for random data).
-// Those candidates are gathered in LDS and each one's rank is counted exactly; if
-// there are too many (heavy ties), K rounds of wave arg-max take the K best instead.
+// wave_topk works on 64-bit keys (the value's order-preserving bits above the
+// complemented id, so one unsigned compare orders by value, then smaller id): the
+// K-th largest lane maximum bounds the top K from below, the keys above that bound
+// are gathered in LDS, and each one's rank is counted exactly (topk_device.h).
 #include "topk_device.h"
 
 namespace ddt {
@@ -67,11 +66,13 @@ topk_partial(const float* __restrict__ logits, int64_t stride, int vocab, int k,
     if (idof(e) != INT_MAX) se += __builtin_amdgcn_exp2f((v[e] - M) * kLog2e);
   const double S = wave_sum((double)se);
 
-  float rv = -INFINITY;
-  int ri = INT_MAX;
-  wave_topk<E>(v, idof, rv, ri, k, sm);
+  unsigned long long key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = pack(v[e], idof(e));  // 0 past the row's end
+  unsigned long long rk = 0ull;
+  wave_topk<E>(key, rk, k, sm);
   const int64_t slot = row * nchunks + c;
-  if (lane < k) cand[slot * k + lane] = pack(rv, ri);
+  if (lane < k) cand[slot * k + lane] = rk;
   if (lane == 0) stats[slot] = make_float2(M, (float)S);
 }
 

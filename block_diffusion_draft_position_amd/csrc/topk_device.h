@@ -17,10 +17,9 @@ constexpr int kCap = 256;  // candidates ranked by counting
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct WaveLds {
-  float cv[kCap];
-  int ci[kCap];
-  float ov[kWave];
-  int oi[kWave];
+  unsigned long long lk[kWave];  // the lanes' largest keys
+  unsigned long long ck[kCap];   // candidates
+  unsigned long long ok[kWave];  // the top K in rank order
 };
 
 // Orders LDS traffic among the lanes of one wave (all the top-K code needs): the
@@ -34,7 +33,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // order-preserving map of a float to uint32
 __device__ __forceinline__ unsigned fkey(float v) {
-  const unsigned b = __builtin_bit_cast(unsigned, v);
+  const unsigned b = __builtin_bit_cast(unsigned, v + 0.f);  // -0 -> +0
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
@@ -51,143 +50,160 @@ __device__ __forceinline__ void unpack(unsigned long long key, float& v, int& id
   id = key ? (int)(0xffffffffu - (unsigned)(key & 0xffffffffull)) : INT_MAX;
 }
 
-// Top-K of the wave's values: E per lane, v[e] with id idof(e) (INT_MAX = none),
-// plus one carried entry (rv, ri) per lane.  On return lane i < K holds the i-th
-// best in (rv, ri); other lanes hold (-inf, INT_MAX).  Ids must be distinct.
-template <int E, typename IdOf>
-__device__ void wave_topk(const float (&v)[E], IdOf idof, float& rv, int& ri, int K, WaveLds& sm) {
-  const int lane = lane_id();
-  const unsigned rk = ri != INT_MAX ? fkey(rv) : 0u;
-  unsigned mk = rk;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (idof(e) != INT_MAX) mk = max(mk, fkey(v[e]));
-  // t = the largest key with at least K lanes whose maximum reaches it
-  unsigned t = 0;
-  for (int b = 31; b >= 0; --b) {
-    const unsigned c = t | (1u << b);
-    if (__popcll(ballot(mk >= c)) >= K) t = c;
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), lane);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#define DDT_MAXSTEP(S)                                                                        \
+  {                                                                                           \
+    const unsigned lo = (unsigned)xchg<S>((int)(unsigned)v);                                  \
+    const unsigned hi = (unsigned)xchg<S>((int)(unsigned)(v >> 32));                          \
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;                         \
+    v = o > v ? o : v;                                                                        \
   }
-  t = max(t, 1u);
+  DDT_MAXSTEP(1) DDT_MAXSTEP(2) DDT_MAXSTEP(4) DDT_MAXSTEP(8) DDT_MAXSTEP(16) DDT_MAXSTEP(32)
+#undef DDT_MAXSTEP
+  return v;
+}
+
+// Top-K of the wave's keys: E per lane (0 = none) plus one carried key rk per lane.
+// Keys are unique (they embed the id), so every rank below is exact.  On return
+// lane i < K holds the i-th largest key in rk; other lanes hold 0.
+//
+// A single wave pays a full pipeline latency for each dependent step, so the
+// selection counts ranks with independent compares against broadcast LDS reads:
+//   1. t = the K-th largest lane maximum: each lane counts the maxima above its own.
+//      At least K keys reach t, so the top K all do; usually few others do (about
+//      K ln(64 / (64 - K)) for random data).
+//   2. the keys >= t are gathered in LDS and each counts the candidates above it;
+//      its count is its rank.
+//   More than kCap candidates (adversarial layouts) falls back to K rounds of a
+//   wave-wide maximum.
+template <int E>
+__device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long& rk, int K,
+                          WaveLds& sm) {
+  const int lane = lane_id();
+  unsigned long long mk = rk;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mk = key[e] > mk ? key[e] : mk;
+  sm.lk[lane] = mk;
+  wave_lds_sync();
+  int above = 0;
+#pragma unroll 8
+  for (int j = 0; j < kWave; j += 2) {
+    const ulonglong2 x = *reinterpret_cast<const ulonglong2*>(&sm.lk[j]);
+    above += (x.x > mk) + (x.y > mk);
+  }
+  // non-zero maxima are unique, so exactly one has rank K-1 when K lanes hold keys
+  const unsigned long long hit = ballot(mk != 0ull && above == K - 1);
+  const unsigned long long t = hit ? readlane_u64(mk, __ffsll((long long)hit) - 1) : 1ull;
+
   int cnt = rk >= t;
 #pragma unroll
-  for (int e = 0; e < E; ++e) cnt += idof(e) != INT_MAX && fkey(v[e]) >= t;
+  for (int e = 0; e < E; ++e) cnt += key[e] >= t;
   const int incl = wave_scan(cnt);
   const int C = readlane(incl, kWave - 1);
   if (C <= kCap) {
     int o = incl - cnt;
-    if (rk >= t) {
-      sm.cv[o] = rv;
-      sm.ci[o] = ri;
-      ++o;
-    }
+    if (rk >= t) sm.ck[o++] = rk;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (idof(e) != INT_MAX && fkey(v[e]) >= t) {
-        sm.cv[o] = v[e];
-        sm.ci[o] = idof(e);
-        ++o;
-      }
-    // pad to a multiple of 8 so the counting loop below can read 8 at a time
-    const int Cp = (C + 7) & ~7;
-    if (lane < Cp - C) {
-      sm.cv[C + lane] = -INFINITY;
-      sm.ci[C + lane] = INT_MAX;
-    }
+      if (key[e] >= t) sm.ck[o++] = key[e];
+    const int Cp = (C + 1) & ~1;  // the counting loop reads two keys at a time
+    if (lane < Cp - C) sm.ck[C + lane] = 0ull;
     wave_lds_sync();
     for (int i0 = 0; i0 < C; i0 += kWave) {
       const int i = i0 + lane;
-      const float mv = i < C ? sm.cv[i] : -INFINITY;
-      const int mi = i < C ? sm.ci[i] : INT_MAX;
+      const unsigned long long me = i < C ? sm.ck[i] : 0ull;
       int r = 0;
-      for (int j0 = 0; j0 < Cp; j0 += 8) {
-        float jv[8];
-        int ji[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          jv[u] = sm.cv[j0 + u];
-          ji[u] = sm.ci[j0 + u];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) r += better(jv[u], ji[u], mv, mi);
+#pragma unroll 4
+      for (int j = 0; j < Cp; j += 2) {
+        const ulonglong2 x = *reinterpret_cast<const ulonglong2*>(&sm.ck[j]);
+        r += (x.x > me) + (x.y > me);
       }
-      if (i < C && r < K) {
-        sm.ov[r] = mv;
-        sm.oi[r] = mi;
-      }
+      if (i < C && r < K) sm.ok[r] = me;
     }
     wave_lds_sync();
-    const int nout = min(C, K);
-    rv = lane < nout ? sm.ov[lane] : -INFINITY;
-    ri = lane < nout ? sm.oi[lane] : INT_MAX;
-    wave_lds_sync();
+    rk = lane < min(C, K) ? sm.ok[lane] : 0ull;
+    wave_lds_sync();  // sm is free again
   } else {
-    // many values tie at the threshold: take the K best one at a time
-    unsigned long long taken = 0ull;  // bit e: v[e] taken; bit E: the carried entry
-    float outv = -INFINITY;
-    int outi = INT_MAX;
+    unsigned long long taken = 0ull;  // bit e: key[e] taken; bit E: the carried key
+    unsigned long long out = 0ull;
     for (int r = 0; r < K; ++r) {
-      float bv = -INFINITY;
-      int bi = INT_MAX, be = -1;
-      if (ri != INT_MAX && !((taken >> E) & 1ull)) {
-        bv = rv;
-        bi = ri;
-        be = E;
-      }
+      unsigned long long b = ((taken >> E) & 1ull) ? 0ull : rk;
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (!((taken >> e) & 1ull) && idof(e) != INT_MAX && better(v[e], idof(e), bv, bi)) {
-          bv = v[e];
-          bi = idof(e);
-          be = e;
-        }
-      float wv = bv;
-      int wi = bi;
-      wave_argmax(wv, wi);
-      if (wi == INT_MAX) break;  // nothing left anywhere
-      if (be >= 0 && bi == wi) taken |= 1ull << be;
-      if (lane == r) {
-        outv = wv;
-        outi = wi;
+        if (!((taken >> e) & 1ull) && key[e] > b) b = key[e];
+      const unsigned long long w = wave_max_u64(b);
+      if (w == 0ull) break;  // nothing left anywhere
+      if (b == w) {
+        if (rk == w && !((taken >> E) & 1ull)) taken |= 1ull << E;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (key[e] == w) taken |= 1ull << e;
       }
+      if (lane == r) out = w;
     }
-    rv = outv;
-    ri = outi;
+    rk = out;
   }
 }
 
 // One wave merges row `row`'s chunk lists (nchunks * k keys) and statistics: on
 // return lane i < k holds the row's i-th best (rv, ri), and lse its log-sum-exp.
+// The statistics (up to kStat per lane) and the first batch of keys are loaded
+// together, so a row costs one memory latency per batch of 64 * E keys.
 template <int E>
 __device__ void merge_row(int64_t row, int nchunks, int k, const unsigned long long* __restrict__ cand,
                           const float2* __restrict__ stats, WaveLds& sm, float& rv, int& ri,
                           double& lse) {
+  constexpr int kStat = 4;
   const int lane = lane_id();
   const float2* st = stats + row * nchunks;
+  const int n = nchunks * k;
+  const unsigned long long* cr = cand + row * (int64_t)n;
+  float2 sv[kStat];
+#pragma unroll
+  for (int q = 0; q < kStat; ++q) {
+    const int i = q * kWave + lane;
+    sv[q] = i < nchunks ? st[i] : make_float2(-INFINITY, 0.f);
+  }
+  unsigned long long kv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = e * kWave + lane;
+    kv[e] = i < n ? cr[i] : 0ull;
+  }
   float mm = -INFINITY;
-  for (int i = lane; i < nchunks; i += kWave) mm = fmaxf(mm, st[i].x);
+#pragma unroll
+  for (int q = 0; q < kStat; ++q) mm = fmaxf(mm, sv[q].x);
+  for (int i = kStat * kWave + lane; i < nchunks; i += kWave) mm = fmaxf(mm, st[i].x);
   const float MM = wave_max(mm);
   double ss = 0.0;
-  for (int i = lane; i < nchunks; i += kWave) {
+#pragma unroll
+  for (int q = 0; q < kStat; ++q)
+    if (q * kWave + lane < nchunks)
+      ss += (double)sv[q].y * (double)__builtin_amdgcn_exp2f((sv[q].x - MM) * kLog2e);
+  for (int i = kStat * kWave + lane; i < nchunks; i += kWave) {
     const float2 t = st[i];
     ss += (double)t.y * (double)__builtin_amdgcn_exp2f((t.x - MM) * kLog2e);
   }
   lse = (double)MM + log(wave_sum(ss));
 
-  const int n = nchunks * k;
-  const unsigned long long* cr = cand + row * (int64_t)n;
-  rv = -INFINITY;
-  ri = INT_MAX;
+  unsigned long long rk = 0ull;
   for (int b0 = 0; b0 < n; b0 += kWave * E) {
-    float v[E];
-    int id[E];
+    if (b0 > 0) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = b0 + e * kWave + lane;
-      unpack(i < n ? cr[i] : 0ull, v[e], id[e]);
+      for (int e = 0; e < E; ++e) {
+        const int i = b0 + e * kWave + lane;
+        kv[e] = i < n ? cr[i] : 0ull;
+      }
     }
-    wave_topk<E>(v, [&](int e) { return id[e]; }, rv, ri, k, sm);
+    wave_topk<E>(kv, rk, k, sm);
   }
+  unpack(rk, rv, ri);
 }
 
 }  // namespace topk

@@ -12,7 +12,8 @@
 //   ancestor bitmask.  Each split leaves an unnormalised partial (O, running max, sum)
 //   per row; attn_combine merges them in log-sum-exp form (deterministic, no atomics).
 //
-//   Per wave and 32-key half-tile, with the MFMA v_mfma_f32_32x32x16_bf16:
+//   attn_partial_bf16 (D = 32, 64): per wave and 32-key half-tile, with the MFMA
+//   v_mfma_f32_32x32x16_bf16 and register-staged tiles:
 //     S^T[key][query] = K[key][:] . Q[query][:]          (D/16 MFMAs)
 //     O^T[d][query]  += V^T[d][key] . P^T[key][query]     (2 * D/32 MFMAs)
 //   Computing the transposes puts one query column in each lane (lanes l and l+32
@@ -22,6 +23,13 @@
 //   k(b, 8h + j) = 16b + 8(j / 4) + 4h + j % 4, and V^T is read in that order).
 //   V is stored transposed in LDS (d-major) so that operand is two 8-byte reads.
 //   Online softmax runs in base 2 with scale * log2(e) folded into one multiply.
+//
+//   attn_d128 (D = 128): 32 query rows per wave as two blocks of 16, K/V tiles moved
+//   global -> LDS by DMA through a 4-stage ring, v_mfma_f32_16x16x32_bf16 for both
+//   products, V^T read with the transposing LDS load (details at the kernel).
+//
+//   Partials are written with nontemporal stores: the combine reads each once, and
+//   keeping them out of the L2 keeps the end-of-kernel cache writeback short.
 //
 // fp32 path: one wave per query row over all of its keys (no splits), VALU only.
 #include <hip/hip_ext.h>
@@ -36,6 +44,8 @@ typedef __bf16 bf16_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kTile = 64;         // keys per LDS tile
@@ -304,11 +314,12 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int d = db * 32 + 8 * qq + 4 * h2;
-        *reinterpret_cast<float4*>(orow + d) =
-            make_float4(oacc[db][4 * qq], oacc[db][4 * qq + 1], oacc[db][4 * qq + 2], oacc[db][4 * qq + 3]);
+        __builtin_nontemporal_store(
+            f32x4{oacc[db][4 * qq], oacc[db][4 * qq + 1], oacc[db][4 * qq + 2], oacc[db][4 * qq + 3]},
+            reinterpret_cast<f32x4*>(orow + d));
       }
     }
-    if (h2 == 0) mlpart[urow] = make_float2(m_run, l_tot);
+    if (h2 == 0) __builtin_nontemporal_store(f32x2{m_run, l_tot}, reinterpret_cast<f32x2*>(mlpart + urow));
   }
 }
 
@@ -326,38 +337,35 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 //     share every K/V fragment read from LDS).
 //   * The running max is raised only when a tile's max exceeds it by more than
 //     2^8; otherwise O and l are not rescaled (p <= 2^8 stays exact in fp32/bf16).
-typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void glob_void;
 
-constexpr int kStages = 4;
+constexpr int kStages = 2;
 constexpr int kTileBytes = kTile * 128 * 2;      // one K or V tile, D = 128
 constexpr float kTau = 8.f;                      // lazy-rescale slack (base-2 units)
 
-// The ring: one statically allocated K and V buffer per stage.  Separate objects let
+// The ring: two stages of one K and one V tile each, 64 KB, so two workgroups fit in a
+// CU's LDS.  Two co-resident workgroups run their phases (LDS reads, MFMA, the exp of
+// the softmax) out of step with each other, which overlaps them on every SIMD better
+// than deeper prefetch within one workgroup does (measured on C2, C3 and C4 shapes).
+// One statically allocated K and V buffer per stage.  Separate objects let
 // the compiler see that a stage being read does not alias the stages still being
 // filled, so it keeps the explicit per-stage vmcnt waits instead of draining all
 // outstanding loads before every LDS read.
 __shared__ __align__(16) unsigned char g_ring_k0[kTileBytes], g_ring_v0[kTileBytes];
 __shared__ __align__(16) unsigned char g_ring_k1[kTileBytes], g_ring_v1[kTileBytes];
-__shared__ __align__(16) unsigned char g_ring_k2[kTileBytes], g_ring_v2[kTileBytes];
-__shared__ __align__(16) unsigned char g_ring_k3[kTileBytes], g_ring_v3[kTileBytes];
 
 template <int ST>
 __device__ __forceinline__ unsigned char* ring_k() {
   if constexpr (ST == 0) return g_ring_k0;
   if constexpr (ST == 1) return g_ring_k1;
-  if constexpr (ST == 2) return g_ring_k2;
-  if constexpr (ST == 3) return g_ring_k3;
 }
 template <int ST>
 __device__ __forceinline__ unsigned char* ring_v() {
   if constexpr (ST == 0) return g_ring_v0;
   if constexpr (ST == 1) return g_ring_v1;
-  if constexpr (ST == 2) return g_ring_v2;
-  if constexpr (ST == 3) return g_ring_v3;
 }
 
 // Slot swizzle of a key row (a bijection on 0..15): the sixteen K rows read by one
@@ -368,7 +376,7 @@ __device__ __forceinline__ unsigned char* ring_v() {
 __device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
 
 template <int NW>
-__global__ void __launch_bounds__(NW * 64, 1)
+__global__ void __launch_bounds__(NW * 64, NW <= 4 ? 2 : 1)
 attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
           const bf16_t* __restrict__ vc, const int64_t* __restrict__ cu_prefix,
           const bf16_t* __restrict__ kt, const bf16_t* __restrict__ vt,
@@ -386,6 +394,9 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int lane = tid % 64;
   const int g4 = lane / 16;   // 16-lane group
   const int l16 = lane % 16;
+  // a wave whose 32 rows all lie past R (the last row group of a unit holds only the
+  // remainder) issues its share of the tile loads and meets the barriers, no more
+  const bool live = (u.rg * NW + wave) * 32 < R;
 
   const int nn = num_nodes[u.s];
   const int64_t p0 = cu_prefix[u.s];
@@ -482,19 +493,13 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 
   // ---- one tile from ring stage ST
   auto step = [&]<int ST>(int t) {
-    // wait for this wave's loads of tile t (tiles t+1, t+2 may stay in flight).
-    // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at max.
-    constexpr int kV1 = NLOAD < 63 ? NLOAD : 63;
-    constexpr int kV2 = 2 * NLOAD < 63 ? 2 * NLOAD : 63;
-    const int ahead = min(ntiles - 1 - t, kStages - 2);
-    if (tree || ahead <= 0) __builtin_amdgcn_s_waitcnt(0x0f70);
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt((kV1 & 0xf) | ((kV1 >> 4) << 14) | 0x0f70);
-    else __builtin_amdgcn_s_waitcnt((kV2 & 0xf) | ((kV2 >> 4) << 14) | 0x0f70);
-    // execution barrier only: every wave has waited for its own loads of tile t
-    // (a __syncthreads fence would also drain the tiles still in flight); the stage
-    // refilled next was read one barrier ago
+    // wait for this wave's loads of tile t: the only loads in flight (expcnt and
+    // lgkmcnt left at their maxima), then an execution barrier only: every wave has
+    // waited for its own loads, and the stage refilled next was read one barrier ago
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     __builtin_amdgcn_s_barrier();
-    if (t + kStages - 1 < ntiles) issue.template operator()<(ST + kStages - 1) % kStages>(t + kStages - 1);
+    if (t + 1 < ntiles) issue.template operator()<ST ^ 1>(t + 1);
+    if (!live) return;
 
     // Per-lane offsets are re-materialised in every step (an empty asm hides their
     // loop invariance); otherwise the compiler keeps one copy per ring stage live.
@@ -628,22 +633,13 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
         lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][kh], lacc[qb], 0, 0, 0);
   };
 
-  // prologue: tiles 0..2 in flight
+  // prologue: tile 0 in flight.  Tile t uses stage t % 2; the loop is unrolled by the
+  // ring depth so every stage is a distinct object at compile time.
   if (0 < ntiles) issue.template operator()<0>(0);
-  if (1 < ntiles) issue.template operator()<1>(1);
-  if (2 < ntiles) issue.template operator()<2>(2);
-  // tile t uses stage t % 4; the loop is unrolled by the ring depth so every stage is
-  // a distinct object at compile time
   if (0 < ntiles) step.template operator()<0>(0);
-  for (int t = 1; t < ntiles; t += 2 * kStages) {
+  for (int t = 1; t < ntiles; t += kStages) {
     step.template operator()<1>(t);
-    if (t + 1 < ntiles) step.template operator()<2>(t + 1);
-    if (t + 2 < ntiles) step.template operator()<3>(t + 2);
-    if (t + 3 < ntiles) step.template operator()<0>(t + 3);
-    if (t + 4 < ntiles) step.template operator()<1>(t + 4);
-    if (t + 5 < ntiles) step.template operator()<2>(t + 5);
-    if (t + 6 < ntiles) step.template operator()<3>(t + 6);
-    if (t + 7 < ntiles) step.template operator()<0>(t + 7);
+    if (t + 1 < ntiles) step.template operator()<0>(t + 1);
   }
 
   // ---- partial results of this split
@@ -655,17 +651,18 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       float* orow = opart + urow * D;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        *reinterpret_cast<float4*>(orow + db * 16 + g4 * 4) =
-            make_float4(oacc[qb][db][0], oacc[qb][db][1], oacc[qb][db][2], oacc[qb][db][3]);
-      if (g4 == 0) mlpart[urow] = make_float2(m_run[qb], lt);
+        __builtin_nontemporal_store(oacc[qb][db], reinterpret_cast<f32x4*>(orow + db * 16 + g4 * 4));
+      if (g4 == 0) __builtin_nontemporal_store(f32x2{m_run[qb], lt}, reinterpret_cast<f32x2*>(mlpart + urow));
     }
   }
 }
 
 // Merge the splits of each row: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
-// Splits are visited in batches of 8 whose loads are all issued before any is used,
-// so a row costs two memory latencies per 8 splits rather than one per split.
-template <typename OutT, int D>
+// The splits are read in batches of KB whose loads are all issued before any is
+// used, and the batches are merged online (running max, rescaled sums), so a row
+// costs one memory latency per KB splits.  The host picks KB >= the split count
+// where it can, making the whole merge one latency.
+template <typename OutT, int D, int KB>
 __global__ void __launch_bounds__(256)
 attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
              const int64_t* __restrict__ cu_prefix, const int32_t* __restrict__ num_nodes, int S,
@@ -673,7 +670,6 @@ attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
              bool has_cache, OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int TPR = D / 4;            // threads per row, 4 outputs each
   constexpr int RPB = 256 / TPR;        // rows per block
-  constexpr int kB = 8;                 // splits per batch
   const int64_t rid = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int dq = (threadIdx.x % TPR) * 4;
   if (rid >= (int64_t)S * N * Hq) return;
@@ -696,41 +692,41 @@ attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
   const int nused = nvalid + 1;
   auto split_of = [&](int i) { return i < nvalid ? i : nsplit; };
   float M = -INFINITY;
-  for (int i0 = 0; i0 < nused; i0 += kB) {
-    float m[kB];
-#pragma unroll
-    for (int b = 0; b < kB; ++b)
-      m[b] = i0 + b < nused ? mlpart[(base + split_of(i0 + b)) * rows_pad + row].x : -INFINITY;
-#pragma unroll
-    for (int b = 0; b < kB; ++b) M = fmaxf(M, m[b]);
-  }
   float l = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0; i0 < nused; i0 += kB) {
-    float2 ml[kB];
-    float4 v[kB];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < nused; i0 += KB) {
+    float2 ml[KB];
+    f32x4 v[KB];
 #pragma unroll
-    for (int b = 0; b < kB; ++b) {
+    for (int b = 0; b < KB; ++b) {
       const bool ok = i0 + b < nused;
       const int64_t ur = (base + split_of(ok ? i0 + b : 0)) * rows_pad + row;
       ml[b] = ok ? mlpart[ur] : make_float2(-INFINITY, 0.f);
-      v[b] = ok ? *reinterpret_cast<const float4*>(opart + ur * D + dq) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[b] = ok ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(opart + ur * D + dq))
+                : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    float bm = M;
 #pragma unroll
-    for (int b = 0; b < kB; ++b) {
+    for (int b = 0; b < KB; ++b) bm = fmaxf(bm, ml[b].x);
+    if (bm == -INFINITY) continue;  // nothing visible yet (cannot happen: the root sees itself)
+    if (M != -INFINITY && M != bm) {
+      const float r = __builtin_amdgcn_exp2f(M - bm);
+      l *= r;
+      acc *= r;
+    }
+    M = bm;
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
       const float w = (ml[b].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[b].x - M);
       l += w * ml[b].y;
-      acc.x += w * v[b].x;
-      acc.y += w * v[b].y;
-      acc.z += w * v[b].z;
-      acc.w += w * v[b].w;
+      acc += w * v[b];
     }
   }
   const float inv = 1.f / l;
-  o[0] = (OutT)(acc.x * inv);
-  o[1] = (OutT)(acc.y * inv);
-  o[2] = (OutT)(acc.z * inv);
-  o[3] = (OutT)(acc.w * inv);
+  o[0] = (OutT)(acc[0] * inv);
+  o[1] = (OutT)(acc[1] * inv);
+  o[2] = (OutT)(acc[2] * inv);
+  o[3] = (OutT)(acc[3] * inv);
   if (lse && dq == 0) lse[rid] = (M + __log2f(l)) * kLn2;
 }
 
@@ -919,22 +915,39 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_
     return p;
   }
   if (D == 128) {
-    // attn_d128: 32 rows per wave, up to 8 waves per workgroup (more would spill)
-    const int waves = (int)ceil_div(ceil_div(p.R, 16), 2);
-    p.row_groups = (int)ceil_div(waves, 8);
-    p.waves = (int)ceil_div(waves, p.row_groups);
+    // attn_d128, 32 rows per wave.  Wide groups (up to 8 waves, one workgroup per CU)
+    // when the whole grid fits on the CUs at once, which is the latency-bound case;
+    // otherwise groups of up to 4 waves, two workgroups per CU.
+    const int waves = (int)ceil_div(p.R, 32);
+    const int rg_wide = (int)ceil_div(waves, 8);
+    const int64_t units_wide = (int64_t)S * Hkv * rg_wide;
+    const int64_t maxp = std::max<int64_t>(max_prefix, 0);
+    const int64_t want = std::max<int64_t>(1, ceil_div(2 * (int64_t)cu_count(), units_wide));
+    const int64_t chunk_w = std::max<int64_t>(
+        (int64_t)align_up((size_t)std::max<int64_t>(1, ceil_div(maxp, want)), kTile), kTile);
+    const int64_t splits_w = std::max<int64_t>(1, ceil_div(maxp, chunk_w)) + 1;
+    if (units_wide * splits_w <= cu_count()) {
+      p.row_groups = rg_wide;
+      p.waves = (int)ceil_div(waves, rg_wide);
+    } else {
+      p.waves = waves < 4 ? waves : 4;
+      p.row_groups = (int)ceil_div(waves, p.waves);
+    }
   } else {
     const int tiles = (int)ceil_div(p.R, 32);
     p.row_groups = (int)ceil_div(tiles, 8);
     p.waves = (int)ceil_div(tiles, p.row_groups);
   }
   p.rows_pad = p.row_groups * p.waves * 32;
+  // prefix splits: about three (sequence, KV head, row group) units per CU (measured
+  // best on C2 and C3 shapes against two and four), and no split above 16K keys so
+  // that unequal prefix lengths still spread evenly
   const int64_t units_base = (int64_t)S * Hkv * p.row_groups;
-  const int64_t target = 2 * (int64_t)cu_count();
+  const int64_t target = (D == 128 ? 3 : 2) * (int64_t)cu_count();
   const int64_t maxp = std::max<int64_t>(max_prefix, 0);
   const int64_t want = std::max<int64_t>(1, ceil_div(target, units_base));
   int64_t chunk = (int64_t)align_up((size_t)std::max<int64_t>(1, ceil_div(maxp, want)), kTile);
-  chunk = std::max<int64_t>(chunk, kTile);
+  chunk = std::min<int64_t>(std::max<int64_t>(chunk, kTile), 16384);
   p.chunk = chunk;
   p.nsplit = (int)std::max<int64_t>(1, ceil_div(maxp, chunk));
   const size_t rows = (size_t)S * Hkv * (p.nsplit + 1) * p.rows_pad;
@@ -983,11 +996,22 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   const int64_t total = (int64_t)S * N * Hq;
   const int rpb = 256 / (D / 4);
   const unsigned blocks = (unsigned)ceil_div(total, rpb);
-#define DDT_COMB(DD)                                                                             \
-  case DD:                                                                                       \
-    hipLaunchKernelGGL((attn_combine<bf16_t, DD>), dim3(blocks), dim3(256), 0, st, opart, ml,    \
-                       cu_prefix, num_nodes, S, N, Hq, Hkv, p.G, p.rows_pad, p.nsplit, p.chunk, \
-                       kc != nullptr, (bf16_t*)out, lse);                                        \
+  // splits per batch: enough for every split of a row when that fits in registers
+  const int nused = p.nsplit + 1;
+  const int kb = nused <= 2 ? 2 : nused <= 4 ? 4 : nused <= 8 ? 8 : nused <= 16 ? 16 : 32;
+#define DDT_COMB_KB(DD, KK)                                                                          \
+  hipLaunchKernelGGL((attn_combine<bf16_t, DD, KK>), dim3(blocks), dim3(256), 0, st, opart, ml,      \
+                     cu_prefix, num_nodes, S, N, Hq, Hkv, p.G, p.rows_pad, p.nsplit, p.chunk,        \
+                     kc != nullptr, (bf16_t*)out, lse)
+#define DDT_COMB(DD)                                     \
+  case DD:                                               \
+    switch (kb) {                                        \
+      case 2: DDT_COMB_KB(DD, 2); break;                 \
+      case 4: DDT_COMB_KB(DD, 4); break;                 \
+      case 8: DDT_COMB_KB(DD, 8); break;                 \
+      case 16: DDT_COMB_KB(DD, 16); break;               \
+      default: DDT_COMB_KB(DD, 32); break;               \
+    }                                                    \
     break;
   switch (D) {
     DDT_COMB(32) DDT_COMB(64) DDT_COMB(128)
@@ -995,6 +1019,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
       return hipErrorInvalidValue;
   }
 #undef DDT_COMB
+#undef DDT_COMB_KB
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // order-preserving map of a float to uint32
 __device__ __forceinline__ unsigned fkey(float v) {
-  const unsigned b = __builtin_bit_cast(unsigned, v);
+  const unsigned b = __builtin_bit_cast(unsigned, v + 0.f);  // -0 -> +0: they compare equal
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
