@@ -17,7 +17,6 @@ constexpr int kCap = 256;  // candidates ranked by counting
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct WaveLds {
-  unsigned long long lk[kWave];  // the lanes' largest keys
   unsigned long long ck[kCap];   // candidates
   unsigned long long ok[kWave];  // the top K in rank order
 };
@@ -73,11 +72,12 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 // Keys are unique (they embed the id), so every rank below is exact.  On return
 // lane i < K holds the i-th largest key in rk; other lanes hold 0.
 //
-// A single wave pays a full pipeline latency for each dependent step, so the
-// selection counts ranks with independent compares against broadcast LDS reads:
-//   1. t = the K-th largest lane maximum: each lane counts the maxima above its own.
-//      At least K keys reach t, so the top K all do; usually few others do (about
-//      K ln(64 / (64 - K)) for random data).
+// A single wave pays a full pipeline latency for each dependent step (about 40 cycles
+// for a VALU op, 70 for a ballot and popcount) and about 8 cycles per independent
+// VALU op, so each stage below is kept to a few dependent steps:
+//   1. t bounds the K-th largest lane maximum from below (a ballot search on the value
+//      bits).  At least K keys reach t, so the top K all do; usually few others do
+//      (about K ln(64 / (64 - K)) for random data).
 //   2. the keys >= t are gathered in LDS and each counts the candidates above it;
 //      its count is its rank.
 //   More than kCap candidates (adversarial layouts) falls back to K rounds of a
@@ -89,17 +89,32 @@ __device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long
   unsigned long long mk = rk;
 #pragma unroll
   for (int e = 0; e < E; ++e) mk = key[e] > mk ? key[e] : mk;
-  sm.lk[lane] = mk;
-  wave_lds_sync();
-  int above = 0;
-#pragma unroll 8
-  for (int j = 0; j < kWave; j += 2) {
-    const ulonglong2 x = *reinterpret_cast<const ulonglong2*>(&sm.lk[j]);
-    above += (x.x > mk) + (x.y > mk);
+  // t: the largest 64-bit key whose upper half at least K lane maxima reach, found two
+  // bits at a time on the upper halves (the value bits; three independent ballots per
+  // step).  Once exactly K lanes reach it no larger threshold keeps K, so the search
+  // stops there.
+  const unsigned mh = (unsigned)(mk >> 32);
+  unsigned th = 0;
+  for (int b = 30; b >= 0; b -= 2) {
+    const unsigned c1 = th | (1u << b), c2 = th | (2u << b), c3 = th | (3u << b);
+    const int n1 = __popcll(ballot(mh >= c1));
+    const int n2 = __popcll(ballot(mh >= c2));
+    const int n3 = __popcll(ballot(mh >= c3));
+    int n = K + 1;
+    if (n3 >= K) {
+      th = c3;
+      n = n3;
+    } else if (n2 >= K) {
+      th = c2;
+      n = n2;
+    } else if (n1 >= K) {
+      th = c1;
+      n = n1;
+    }
+    if (n == K) break;
   }
-  // non-zero maxima are unique, so exactly one has rank K-1 when K lanes hold keys
-  const unsigned long long hit = ballot(mk != 0ull && above == K - 1);
-  const unsigned long long t = hit ? readlane_u64(mk, __ffsll((long long)hit) - 1) : 1ull;
+  // keys are non-zero exactly when present; with fewer than K present lanes th stays 0
+  const unsigned long long t = th ? (unsigned long long)th << 32 : 1ull;
 
   int cnt = rk >= t;
 #pragma unroll

@@ -601,7 +601,7 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     // ---- O^T += V^T . P^T  (V^T read transposed from the row-major tile).  The two
     // key rows a lane addresses (vrow, vrow + 16, plus 32 per key half) share one
     // swizzle, so the chunk slot is (2 db) ^ vsw_hi | vsw_lo.
-    // The fragments of head-dim block db + 1 are read while block db's MFMAs run.
+    // The fragments of head-dim block db + 2 are read while block db's MFMAs run.
     auto vread = [&](int db, bf16x8 (&a)[2]) {
       const int slot = (((2 * db) ^ vhi) | vlo) << 4;
 #pragma unroll
@@ -612,17 +612,18 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
         a[kh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
-    bf16x8 va[2][2];
+    bf16x8 va[3][2];
     vread(0, va[0]);
+    vread(1, va[1]);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      if (db + 1 < 8) vread(db + 1, va[(db + 1) & 1]);
+      if (db + 2 < 8) vread(db + 2, va[(db + 2) % 3]);
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db & 1][kh], pb[qb][kh], oacc[qb][db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);  // V fragments of two blocks live at most
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db % 3][kh], pb[qb][kh], oacc[qb][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // V fragments of three blocks live at most
     }
     // sum_k P[k][q] for every query: the same contraction with V replaced by ones
     // (the sum is of the bf16 weights the numerator uses)
