@@ -28,7 +28,7 @@
 namespace ddt {
 namespace {
 
-template <int J, bool SK>
+template <int J, int SK>
 __global__ void __launch_bounds__(kWave)
 build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict__ topk_logq,
                   const int32_t* __restrict__ bonus, int L, int K, int B,
@@ -56,7 +56,7 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
   if (lane == 0) num_nodes[s] = n;
 }
 
-template <int J, bool SK>
+template <int J, int SK>
 hipError_t launch_jk(const int32_t* tok, const float* logq, const int32_t* bonus, int S, int L,
                      int K, int B, int32_t* tree_tok, int32_t* parent, int32_t* depth,
                      float* node_logq, int32_t* num_nodes, hipStream_t st) {
@@ -77,12 +77,15 @@ hipError_t launch_j(const int32_t* tok, const float* logq, const int32_t* bonus,
                     int K, int B, int32_t* tree_tok, int32_t* parent, int32_t* depth,
                     float* node_logq, int32_t* num_nodes, hipStream_t st) {
   if constexpr (J <= 2) {
-    if (K <= 16)
-      return launch_jk<J, true>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq,
-                                num_nodes, st);
-  }
-  return launch_jk<J, false>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq,
+    if (K <= 8)
+      return launch_jk<J, 8>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq,
                              num_nodes, st);
+    if (K <= 16)
+      return launch_jk<J, 16>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq,
+                              num_nodes, st);
+  }
+  return launch_jk<J, 0>(tok, logq, bonus, S, L, K, B, tree_tok, parent, depth, node_logq,
+                         num_nodes, st);
 }
 
 }  // namespace

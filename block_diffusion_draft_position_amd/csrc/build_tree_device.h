@@ -12,6 +12,7 @@ namespace ddt {
 namespace tree {
 
 constexpr int kRankCap = 256;  // final rounds with at most this many candidates rank them exactly
+constexpr unsigned long long kIdxMask = 0x3ffull;  // low key bits that carry the node-order number
 
 struct TreeSmem {
   unsigned long long* key;  // [kRankCap] final-round candidate keys
@@ -123,9 +124,10 @@ __device__ inline TreeSmem carve(unsigned char* p, int N, int LK) {
 // [L, K] top-K log-probabilities and tokens.  Writes the N-entry output rows (node_logq
 // and pos_ids may be null; pos_ids gets P + depth) and sm.cpar, and returns num_nodes.  sync() orders the wave's LDS
 // traffic: a workgroup barrier when the wave is alone, a wave barrier otherwise.
-// J register slots of streams per lane; SK (K <= 16 and J <= 2) caches each stream's
-// logq row in registers for the round, so its reads are issued together.
-template <int J, bool SK, typename Sync>
+// J register slots of streams per lane.  SK > 0 (K <= SK, SK = 8 or 16, J <= 2) caches
+// each stream's logq row in SK registers for the round, so its reads are issued
+// together and the per-rank loops run SK steps.
+template <int J, int SK, typename Sync>
 __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
                      int32_t* __restrict__ tree_tok, int32_t* __restrict__ tree_parent,
                      int32_t* __restrict__ tree_depth, float* __restrict__ node_logq,
@@ -160,13 +162,14 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
 
   // candidates of stream j scoring above th: a prefix of the stream.  Small K reads
   // the whole row at once; larger K bisects.
-  float rowv[SK ? J : 1][16];  // SK: this round's logq row of each stream
+  constexpr int KW = SK > 0 ? SK : 1;
+  float rowv[SK ? J : 1][KW];  // SK: this round's logq row of each stream
   auto above = [&](int j, double th) -> int {
     if (cur[j] >= K) return 0;
-    if constexpr (SK) {
+    if constexpr (SK > 0) {
       int c = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < KW; ++r)
         if (r < K && r >= cur[j]) c += sc[j] + (double)rowv[j][r] > th;
       return c;
     }
@@ -191,13 +194,13 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
   int n = 1;  // nodes selected so far, root included
   while (n - 1 < B) {
     const int R = B - (n - 1);
-    if constexpr (SK) {
+    if constexpr (SK > 0) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const bool open = cur[j] < K;
         const int rb = (open ? dep[j] : 0) * K;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) rowv[j][r] = (open && r < K) ? sm.lq[rb + r] : -INFINITY;
+        for (int r = 0; r < KW; ++r) rowv[j][r] = (open && r < K) ? sm.lq[rb + r] : -INFINITY;
       }
     }
     bool live = false;
@@ -246,51 +249,99 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
           base += readlane(incl, kWave - 1);
         }
       }
+      // Candidate keys: the score's order-preserving 64 bits with the lowest ten replaced
+      // by the complement of the candidate's node-order number, so keys are unique and
+      // scores that tie (to 2^-42 relative) go in node order.
+      // candidate i of stream j (rank cur + i) scoring v
+      auto ukey = [&](int j, int i, double v) -> unsigned long long {
+        return (key_of(v) & ~kIdxMask) | (kIdxMask - (unsigned long long)(off[j] + i));
+      };
       if (total <= kRankCap) {
-        // exact ranks: larger key first, equal keys in node order
-        if constexpr (SK) {
-#pragma unroll
-          for (int j = 0; j < J; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (r >= cur[j] && r < cur[j] + cnt[j])
-                sm.key[off[j] + r - cur[j]] = key_of(sc[j] + (double)rowv[j][r]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < J; ++j)
-            for (int i = 0; i < cnt[j]; ++i)
-              sm.key[off[j] + i] = key_of(sc[j] + lq(dep[j], cur[j] + i));
-        }
-        const int Tp = (total + 7) & ~7;
-        if (lane < Tp - total) sm.key[total + lane] = 0ull;  // below every real key
-        sync();
-        for (int i0 = 0; i0 < total; i0 += kWave) {
-          const int i = i0 + lane;
-          const unsigned long long mk = i < total ? sm.key[i] : ~0ull;
-          int r = 0;
-          for (int j0 = 0; j0 < Tp; j0 += 8) {
-            unsigned long long kj[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) kj[u] = sm.key[j0 + u];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) r += kj[u] > mk || (kj[u] == mk && j0 + u < i);
-          }
-          if (i < total) sm.sel[i] = r < R;
-        }
-        sync();
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-          int c = 0;
-          if constexpr (SK) {
-            int sv[16];
+          if constexpr (SK > 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sv[i] = i < cnt[j] ? sm.sel[off[j] + i] : 0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) c += sv[i];
+            for (int r = 0; r < KW; ++r)
+              if (r >= cur[j] && r < cur[j] + cnt[j])
+                sm.key[off[j] + r - cur[j]] = ukey(j, r - cur[j], sc[j] + (double)rowv[j][r]);
           } else {
-            for (int i = 0; i < cnt[j]; ++i) c += sm.sel[off[j] + i];
+            for (int i = 0; i < cnt[j]; ++i)
+              sm.key[off[j] + i] = ukey(j, i, sc[j] + lq(dep[j], cur[j] + i));
           }
-          cnt[j] = c;
+        }
+        if (total <= kWave) {
+          // one candidate per lane: the R-th largest key by a ballot search two bits at
+          // a time (three independent ballots per step), stopping once exactly R keys
+          // reach the prefix; each stream then keeps its candidates at or above it
+          sync();
+          const bool has = lane < total;
+          const unsigned long long mk = has ? sm.key[lane] : 0ull;
+          unsigned long long t = 0ull;
+          for (int b = 62; b >= 0; b -= 2) {
+            const unsigned long long c1 = t | (1ull << b), c2 = t | (2ull << b), c3 = t | (3ull << b);
+            const int n1 = __popcll(ballot(has && mk >= c1));
+            const int n2 = __popcll(ballot(has && mk >= c2));
+            const int n3 = __popcll(ballot(has && mk >= c3));
+            int nb = R + 1;
+            if (n3 >= R) {
+              t = c3;
+              nb = n3;
+            } else if (n2 >= R) {
+              t = c2;
+              nb = n2;
+            } else if (n1 >= R) {
+              t = c1;
+              nb = n1;
+            }
+            if (nb == R) break;
+          }
+#pragma unroll
+          for (int j = 0; j < J; ++j) {
+            int c = 0;
+            if constexpr (SK > 0) {
+#pragma unroll
+              for (int r = 0; r < KW; ++r)
+                c += r >= cur[j] && r < cur[j] + cnt[j] &&
+                     ukey(j, r - cur[j], sc[j] + (double)rowv[j][r]) >= t;
+            } else {
+              for (int i = 0; i < cnt[j]; ++i) c += ukey(j, i, sc[j] + lq(dep[j], cur[j] + i)) >= t;
+            }
+            cnt[j] = c;
+          }
+          sync();  // sm.key is read again by the next cut
+        } else {
+          // exact ranks: each candidate counts the keys above its own
+          const int Tp = (total + 7) & ~7;
+          if (lane < Tp - total) sm.key[total + lane] = 0ull;  // below every real key
+          sync();
+          for (int i0 = 0; i0 < total; i0 += kWave) {
+            const int i = i0 + lane;
+            const unsigned long long mk = i < total ? sm.key[i] : ~0ull;
+            int r = 0;
+            for (int j0 = 0; j0 < Tp; j0 += 8) {
+              unsigned long long kj[8];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) kj[u] = sm.key[j0 + u];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) r += kj[u] > mk;
+            }
+            if (i < total) sm.sel[i] = r < R;
+          }
+          sync();
+#pragma unroll
+          for (int j = 0; j < J; ++j) {
+            int c = 0;
+            if constexpr (SK > 0) {
+              int sv[KW];
+#pragma unroll
+              for (int i = 0; i < KW; ++i) sv[i] = i < cnt[j] ? sm.sel[off[j] + i] : 0;
+#pragma unroll
+              for (int i = 0; i < KW; ++i) c += sv[i];
+            } else {
+              for (int i = 0; i < cnt[j]; ++i) c += sm.sel[off[j] + i];
+            }
+            cnt[j] = c;
+          }
         }
       } else {
         // radix select over the 64-bit keys, 8 bits per pass from the first bit where
@@ -399,10 +450,10 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
           }
         }
         const int cn = cur[j] + cnt[j];
-        if constexpr (SK) {
+        if constexpr (SK > 0) {
           float hv = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
+          for (int r = 0; r < KW; ++r)
             if (r == cn) hv = rowv[j][r];
           head[j] = cn < K ? sc[j] + (double)hv : -INFINITY;
         } else {

@@ -22,7 +22,7 @@ __host__ __device__ constexpr int waves_for(int J, int ME) {
   return J >= 16 ? 4 : (J >= 4 || ME == 32) ? 8 : 16;
 }
 
-template <int J, bool SK, int ME>
+template <int J, int SK, int ME>
 __global__ void __launch_bounds__(waves_for(J, ME) * kWave)
 draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __restrict__ stats,
                   int nchunks, const int32_t* __restrict__ bonus,
@@ -77,7 +77,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
   mask::rows(sm.cpar, nn_s, N, W, mask + (int64_t)s * N * W, threadIdx.x, NW * kWave);
 }
 
-template <int J, bool SK, int ME>
+template <int J, int SK, int ME>
 hipError_t launch_jkm(const unsigned long long* cand, const float2* stats, int nchunks,
                       const int32_t* bonus, const int64_t* cu_prefix, int S, int L, int K, int B,
                       int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
@@ -98,20 +98,20 @@ hipError_t launch_jkm(const unsigned long long* cand, const float2* stats, int n
 }
 
 template <int J, int ME>
-hipError_t launch_jm(bool sk, const unsigned long long* cand, const float2* stats, int nchunks,
-                     const int32_t* bonus, const int64_t* cu_prefix, int S, int L, int K, int B,
+hipError_t launch_jm(int K, const unsigned long long* cand, const float2* stats, int nchunks,
+                     const int32_t* bonus, const int64_t* cu_prefix, int S, int L, int B,
                      int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
                      int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
                      int32_t* pos_ids, hipStream_t st) {
+#define DDT_ARGS_SK                                                                         \
+  cand, stats, nchunks, bonus, cu_prefix, S, L, K, B, topk_tok, topk_logq, tree_tok, parent, \
+      depth, node_logq, num_nodes, mask, pos_ids, st
   if constexpr (J <= 2) {
-    if (sk)
-      return launch_jkm<J, true, ME>(cand, stats, nchunks, bonus, cu_prefix, S, L, K, B, topk_tok,
-                                     topk_logq, tree_tok, parent, depth, node_logq, num_nodes,
-                                     mask, pos_ids, st);
+    if (K <= 8) return launch_jkm<J, 8, ME>(DDT_ARGS_SK);
+    if (K <= 16) return launch_jkm<J, 16, ME>(DDT_ARGS_SK);
   }
-  return launch_jkm<J, false, ME>(cand, stats, nchunks, bonus, cu_prefix, S, L, K, B, topk_tok,
-                                  topk_logq, tree_tok, parent, depth, node_logq, num_nodes, mask,
-                                  pos_ids, st);
+  return launch_jkm<J, 0, ME>(DDT_ARGS_SK);
+#undef DDT_ARGS_SK
 }
 
 int slots_for(int B) { return (int)ceil_div(B + 1, kWave); }
@@ -148,10 +148,9 @@ hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t
   float2* stats;
   topk_ws_parts(const_cast<void*>(ws), (int64_t)S * L, K, plan, &cand, &stats);
   const int slots = slots_for(B);
-  const bool sk = K <= 16;
-#define DDT_ARGS                                                                                \
-  sk, cand, stats, plan.nchunks, bonus, cu_prefix, S, L, K, B, topk_tok, topk_logq, tree_tok, \
-      parent, depth, node_logq, num_nodes, mask, pos_ids, st
+#define DDT_ARGS                                                                               \
+  K, cand, stats, plan.nchunks, bonus, cu_prefix, S, L, B, topk_tok, topk_logq, tree_tok, parent, \
+      depth, node_logq, num_nodes, mask, pos_ids, st
 #define DDT_J(JJ)                                                              \
   return plan.merge_e == 8 ? launch_jm<JJ, 8>(DDT_ARGS) : launch_jm<JJ, 32>(DDT_ARGS)
   if (slots <= 1) DDT_J(1);

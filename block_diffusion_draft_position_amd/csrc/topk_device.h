@@ -205,7 +205,9 @@ __device__ void merge_row(int64_t row, int nchunks, int k, const unsigned long l
     const float2 t = st[i];
     ss += (double)t.y * (double)__builtin_amdgcn_exp2f((t.x - MM) * kLog2e);
   }
-  lse = (double)MM + log(wave_sum(ss));
+  // the sum stays fp64; its logarithm is taken in fp32 (one instruction instead of a
+  // long software routine; absolute error about 2e-6 for sums up to 2^31)
+  lse = (double)MM + (double)(__builtin_amdgcn_logf((float)wave_sum(ss)) * 0.6931471805599453f);
 
   unsigned long long rk = 0ull;
   for (int b0 = 0; b0 < n; b0 += kWave * E) {
