@@ -175,6 +175,60 @@ def test_edge_cases(name, kw, fused):
     run_case(cfg, fused=fused)
 
 
+def test_narrow_attention_groups():
+    """A grid too large for one workgroup per CU: 4-wave row groups, two per CU, the last
+    group of each (sequence, KV head) holding only the remainder rows (its other waves
+    idle), ragged prefixes cut into many splits."""
+    cfg = configs.custom("narrow", S=6, L=4, V=500, K=4, B=64, prefix=(900, 3000), Hq=16, Hkv=4,
+                         D=128, dtype="bf16")
+    run_case(cfg, rows_per_seq=240)
+
+
+def test_signed_zero_ties():
+    """-0.0 and +0.0 compare equal, so a tie between them goes to the smaller token id,
+    in the top-K and in the walk's arg-max, as in the oracle."""
+    S, L, V, K, B = 2, 3, 96, 4, 6
+    rng = np.random.default_rng(5)
+    logits = np.full((S, L, V), -4.0, dtype=np.float32)
+    logits += rng.uniform(-0.5, 0.0, size=logits.shape).astype(np.float32)
+    for s in range(S):
+        for i in range(L):
+            ids = rng.choice(V, 3, replace=False)
+            lo, mid, hi = np.sort(ids)
+            logits[s, i, lo] = -0.0
+            logits[s, i, hi] = 0.0
+            logits[s, i, mid] = -0.0
+    bonus = np.array([1, 2], dtype=np.int32)
+    d = dev_tensor(logits)
+    tok, lq = ddt.ddt_topk(d, K)
+    gtok, glq = tok.cpu().numpy(), lq.cpu().numpy()
+    for s in range(S):
+        rt, rl = oracle.topk(logits[s], K)
+        assert np.array_equal(gtok[s], rt), s
+        np.testing.assert_allclose(glq[s], rl, rtol=0, atol=TOPK_ATOL)
+    # the zeros tie exactly, so the tree may order them either way (a tie the synthetic
+    # workloads exclude); the walk is checked on the GPU's own tree on both sides
+    tree = ddt.ddt_build_tree(tok, lq, dev_tensor(bonus), B)
+    gt = {k: v.cpu().numpy() for k, v in tree.items() if v is not None}
+    N = B + 1
+    target = np.full((S, N, V), -3.0, dtype=np.float32)
+    for s in range(S):
+        for n in range(int(gt["num_nodes"][s])):
+            kids = [c for c in range(N) if gt["parent"][s][c] == n]
+            want = int(gt["tree_tok"][s][kids[0]]) if kids else int(rng.integers(V))
+            other = (want + 7) % V
+            lo, hi = min(want, other), max(want, other)
+            target[s, n, lo] = -0.0   # the smaller id holds -0: it must win the tie
+            target[s, n, hi] = 0.0
+    walk = ddt.ddt_tree_walk(tree["tree_tok"], tree["parent"], tree["num_nodes"], dev_tensor(target), L)
+    gw = {k: v.cpu().numpy() for k, v in walk.items()}
+    for s in range(S):
+        w = oracle.tree_walk(gt["tree_tok"][s], gt["parent"][s], int(gt["num_nodes"][s]), target[s], L)
+        assert int(gw["accept_len"][s]) == int(w["accept_len"]), s
+        assert int(gw["bonus"][s]) == int(w["bonus"]), s
+        assert np.array_equal(gw["acc_nodes"][s], w["acc_nodes"]), s
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
 def test_large_budget_multi_word_mask(fused):
     cfg = configs.custom("bigB", S=1, L=8, V=1000, K=16, B=700, prefix=(300, 300), Hq=4, Hkv=1,
