@@ -19,7 +19,7 @@ namespace {
 
 // waves per workgroup: as many merge waves as registers allow next to the builder
 __host__ __device__ constexpr int waves_for(int J, int ME) {
-  return J >= 16 ? 4 : (J >= 4 || ME == 32) ? 8 : 16;
+  return (J >= 16 || ME >= 64) ? 4 : (J >= 4 || ME == 32) ? 8 : 16;
 }
 
 template <int J, int SK, int ME>
@@ -152,7 +152,9 @@ hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t
   K, cand, stats, plan.nchunks, bonus, cu_prefix, S, L, B, topk_tok, topk_logq, tree_tok, parent, \
       depth, node_logq, num_nodes, mask, pos_ids, st
 #define DDT_J(JJ)                                                              \
-  return plan.merge_e == 8 ? launch_jm<JJ, 8>(DDT_ARGS) : launch_jm<JJ, 32>(DDT_ARGS)
+  return plan.merge_e == 8 ? launch_jm<JJ, 8>(DDT_ARGS)    \
+       : plan.merge_e == 32 ? launch_jm<JJ, 32>(DDT_ARGS) \
+                            : launch_jm<JJ, 64>(DDT_ARGS)
   if (slots <= 1) DDT_J(1);
   if (slots <= 2) DDT_J(2);
   if (slots <= 4) DDT_J(4);

@@ -12,9 +12,9 @@
 //                 exp(x - max) (fp32 per lane, fp64 across the wave) and the chunk's
 //                 top-K list (wave_topk below), and writes both to the workspace:
 //                 the list as 64-bit keys, the statistics as a (max, sum) pair.
-//   topk_merge    one wave per row reads every chunk's keys, spread over all 64
-//                 lanes, merges them with the same wave_topk, folds the statistics
-//                 into the log-sum-exp (fp64) and writes tokens and log-probabilities.
+//   topk_merge    one wave per row reads every chunk's list, one list per lane,
+//                 merges them with the same wave_topk, folds the statistics into the
+//                 log-sum-exp (fp64 sum) and writes tokens and log-probabilities.
 //
 // wave_topk works on 64-bit keys (the value's order-preserving bits above the
 // complemented id, so one unsigned compare orders by value, then smaller id): the
@@ -55,15 +55,14 @@ topk_partial(const float* __restrict__ logits, int64_t stride, int vocab, int k,
     const int i = lo + ((e / 4) * kWave + lane) * 4 + e % 4;
     return i < vocab ? i : INT_MAX;
   };
+  // elements past the row's end hold -inf: they add nothing to the maximum or the sum
   float m = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (idof(e) != INT_MAX) m = fmaxf(m, v[e]);
+  for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
   const float M = wave_max(m);
   float se = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (idof(e) != INT_MAX) se += __builtin_amdgcn_exp2f((v[e] - M) * kLog2e);
+  for (int e = 0; e < E; ++e) se += __builtin_amdgcn_exp2f((v[e] - M) * kLog2e);
   const double S = wave_sum((double)se);
 
   unsigned long long key[E];
@@ -109,7 +108,7 @@ TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
     }
   }
   p.nchunks = (int)ceil_div(vocab, (int64_t)kWave * p.e);
-  p.merge_e = (int64_t)p.nchunks * k <= kWave * 8 ? 8 : 32;
+  p.merge_e = k <= 8 ? 8 : k <= 32 ? 32 : 64;  // keys per lane: one chunk list each
   const size_t nslot = (size_t)rows * p.nchunks;
   p.ws_bytes = align_up(nslot * k * sizeof(unsigned long long), 256) +
                align_up(nslot * sizeof(float2), 256);
@@ -152,8 +151,11 @@ hipError_t launch_topk_merge(int64_t rows, int k, int32_t* tok, float* logq, voi
   if (plan.merge_e == 8)
     hipLaunchKernelGGL(topk_merge<8>, dim3((unsigned)rows), dim3(kWave), 0, st, plan.nchunks, k,
                        cand, stt, tok, logq);
-  else
+  else if (plan.merge_e == 32)
     hipLaunchKernelGGL(topk_merge<32>, dim3((unsigned)rows), dim3(kWave), 0, st, plan.nchunks, k,
+                       cand, stt, tok, logq);
+  else
+    hipLaunchKernelGGL(topk_merge<64>, dim3((unsigned)rows), dim3(kWave), 0, st, plan.nchunks, k,
                        cand, stt, tok, logq);
   return hipGetLastError();
 }

@@ -17,7 +17,7 @@ constexpr int kCap = 256;  // candidates ranked by counting
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct WaveLds {
-  unsigned long long ck[kCap];   // candidates
+  unsigned long long ck[kCap + kWave];  // candidates, then one spare slot per lane
   unsigned long long ok[kWave];  // the top K in rank order
 };
 
@@ -68,32 +68,23 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
-// Top-K of the wave's keys: E per lane (0 = none) plus one carried key rk per lane.
-// Keys are unique (they embed the id), so every rank below is exact.  On return
-// lane i < K holds the i-th largest key in rk; other lanes hold 0.
-//
-// A single wave pays a full pipeline latency for each dependent step (about 40 cycles
-// for a VALU op, 70 for a ballot and popcount) and about 8 cycles per independent
-// VALU op, so each stage below is kept to a few dependent steps:
-//   1. t bounds the K-th largest lane maximum from below (a ballot search on the value
-//      bits).  At least K keys reach t, so the top K all do; usually few others do
-//      (about K ln(64 / (64 - K)) for random data).
-//   2. the keys >= t are gathered in LDS and each counts the candidates above it;
-//      its count is its rank.
-//   More than kCap candidates (adversarial layouts) falls back to K rounds of a
-//   wave-wide maximum.
-template <int E>
-__device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long& rk, int K,
-                          WaveLds& sm) {
-  const int lane = lane_id();
-  unsigned long long mk = rk;
-#pragma unroll
-  for (int e = 0; e < E; ++e) mk = key[e] > mk ? key[e] : mk;
-  // t: the largest 64-bit key whose upper half at least K lane maxima reach, found two
-  // bits at a time on the upper halves (the value bits; three independent ballots per
-  // step).  Once exactly K lanes reach it no larger threshold keeps K, so the search
-  // stops there.
-  const unsigned mh = (unsigned)(mk >> 32);
+// The wave-level top-K below works in two stages.  A single wave pays a full pipeline
+// latency for each dependent step (about 40 cycles for a VALU op, 70 for a ballot and
+// popcount) and about 8 cycles per independent VALU op, so each stage is kept to a
+// few dependent steps and little work per element:
+//   1. kth_upper: th bounds the K-th largest lane maximum from below, found on the
+//      upper 32 key bits (the value bits) two bits at a time, three independent ballots
+//      per step, stopping once exactly K lanes reach it.  At least K keys reach th, so
+//      the top K all do; usually few others do (about K ln(64 / (64 - K)) for random
+//      data).
+//   2. rank_select: those candidates are gathered in LDS as 64-bit keys and each counts
+//      the keys above its own, which is its rank (keys are unique: they embed the id).
+//      More than kCap candidates (adversarial layouts) falls back to K rounds of a
+//      wave-wide maximum.
+
+// the largest th (on 32-bit upper key halves) that at least K lanes' mh reach; 0 when
+// fewer than K lanes hold keys
+__device__ __forceinline__ unsigned kth_upper(unsigned mh, int K) {
   unsigned th = 0;
   for (int b = 30; b >= 0; b -= 2) {
     const unsigned c1 = th | (1u << b), c2 = th | (2u << b), c3 = th | (3u << b);
@@ -113,20 +104,33 @@ __device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long
     }
     if (n == K) break;
   }
-  // keys are non-zero exactly when present; with fewer than K present lanes th stays 0
-  const unsigned long long t = th ? (unsigned long long)th << 32 : 1ull;
+  return th;
+}
 
-  int cnt = rk >= t;
+// Top K of the candidates: element e of the lane when cand(e) (its key keyof(e), with
+// valid(e) marking the elements that exist at all), plus the carried key rk when
+// carry.  On return lane i < K holds the i-th largest key in rk; other lanes hold 0.
+template <int E, typename Valid, typename Cand, typename KeyOf>
+__device__ void rank_select(Valid valid, Cand cand, KeyOf keyof, bool carry,
+                            unsigned long long& rk, int K, WaveLds& sm) {
+  const int lane = lane_id();
+  int cnt = carry;
 #pragma unroll
-  for (int e = 0; e < E; ++e) cnt += key[e] >= t;
+  for (int e = 0; e < E; ++e) cnt += cand(e);
   const int incl = wave_scan(cnt);
   const int C = readlane(incl, kWave - 1);
   if (C <= kCap) {
+    // every element is stored, a non-candidate into this lane's spare slot, so the
+    // gather has no branches
     int o = incl - cnt;
-    if (rk >= t) sm.ck[o++] = rk;
+    sm.ck[carry ? o : kCap + lane] = rk;
+    o += carry;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (key[e] >= t) sm.ck[o++] = key[e];
+    for (int e = 0; e < E; ++e) {
+      const bool c = cand(e);
+      sm.ck[c ? o : kCap + lane] = keyof(e);
+      o += c;
+    }
     const int Cp = (C + 1) & ~1;  // the counting loop reads two keys at a time
     if (lane < Cp - C) sm.ck[C + lane] = 0ull;
     wave_lds_sync();
@@ -145,20 +149,20 @@ __device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long
     rk = lane < min(C, K) ? sm.ok[lane] : 0ull;
     wave_lds_sync();  // sm is free again
   } else {
-    unsigned long long taken = 0ull;  // bit e: key[e] taken; bit E: the carried key
+    unsigned long long taken = 0ull;  // bit e: element e taken; bit E: the carried key
     unsigned long long out = 0ull;
     for (int r = 0; r < K; ++r) {
       unsigned long long b = ((taken >> E) & 1ull) ? 0ull : rk;
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (!((taken >> e) & 1ull) && key[e] > b) b = key[e];
+        if (valid(e) && !((taken >> e) & 1ull) && keyof(e) > b) b = keyof(e);
       const unsigned long long w = wave_max_u64(b);
       if (w == 0ull) break;  // nothing left anywhere
       if (b == w) {
         if (rk == w && !((taken >> E) & 1ull)) taken |= 1ull << E;
 #pragma unroll
         for (int e = 0; e < E; ++e)
-          if (key[e] == w) taken |= 1ull << e;
+          if (valid(e) && keyof(e) == w) taken |= 1ull << e;
       }
       if (lane == r) out = w;
     }
@@ -166,10 +170,25 @@ __device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long
   }
 }
 
-// One wave merges row `row`'s chunk lists (nchunks * k keys) and statistics: on
-// return lane i < k holds the row's i-th best (rv, ri), and lse its log-sum-exp.
-// The statistics (up to kStat per lane) and the first batch of keys are loaded
-// together, so a row costs one memory latency per batch of 64 * E keys.
+// Top K of the wave's keys: E per lane (0 = none) plus one carried key rk per lane.
+template <int E>
+__device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long& rk, int K,
+                          WaveLds& sm) {
+  unsigned mh = (unsigned)(rk >> 32);
+#pragma unroll
+  for (int e = 0; e < E; ++e) mh = max(mh, (unsigned)(key[e] >> 32));
+  const unsigned th = kth_upper(mh, K);
+  const unsigned long long t = th ? (unsigned long long)th << 32 : 1ull;
+  rank_select<E>([&](int e) { return key[e] != 0ull; }, [&](int e) { return key[e] >= t; },
+                 [&](int e) { return key[e]; }, rk >= t, rk, K, sm);
+}
+
+// One wave merges row `row`'s chunk lists (nchunks lists of k keys, each sorted best
+// first) and statistics: on return lane i < k holds the row's i-th best (rv, ri), and
+// lse its log-sum-exp.  Lane c holds chunk c's list (E >= k keys; 64 chunks per batch),
+// so a lane's maximum is its chunk's best key and the threshold of wave_topk is the
+// k-th best chunk head: only a handful of keys beyond the top k reach it.  The
+// statistics (up to kStat per lane) and the first batch of keys are loaded together.
 template <int E>
 __device__ void merge_row(int64_t row, int nchunks, int k, const unsigned long long* __restrict__ cand,
                           const float2* __restrict__ stats, WaveLds& sm, float& rv, int& ri,
@@ -177,8 +196,7 @@ __device__ void merge_row(int64_t row, int nchunks, int k, const unsigned long l
   constexpr int kStat = 4;
   const int lane = lane_id();
   const float2* st = stats + row * nchunks;
-  const int n = nchunks * k;
-  const unsigned long long* cr = cand + row * (int64_t)n;
+  const unsigned long long* cr = cand + row * (int64_t)nchunks * k;
   float2 sv[kStat];
 #pragma unroll
   for (int q = 0; q < kStat; ++q) {
@@ -186,11 +204,11 @@ __device__ void merge_row(int64_t row, int nchunks, int k, const unsigned long l
     sv[q] = i < nchunks ? st[i] : make_float2(-INFINITY, 0.f);
   }
   unsigned long long kv[E];
+  auto load = [&](int c) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = e * kWave + lane;
-    kv[e] = i < n ? cr[i] : 0ull;
-  }
+    for (int e = 0; e < E; ++e) kv[e] = (c < nchunks && e < k) ? cr[(int64_t)c * k + e] : 0ull;
+  };
+  load(lane);
   float mm = -INFINITY;
 #pragma unroll
   for (int q = 0; q < kStat; ++q) mm = fmaxf(mm, sv[q].x);
@@ -210,14 +228,8 @@ __device__ void merge_row(int64_t row, int nchunks, int k, const unsigned long l
   lse = (double)MM + (double)(__builtin_amdgcn_logf((float)wave_sum(ss)) * 0.6931471805599453f);
 
   unsigned long long rk = 0ull;
-  for (int b0 = 0; b0 < n; b0 += kWave * E) {
-    if (b0 > 0) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = b0 + e * kWave + lane;
-        kv[e] = i < n ? cr[i] : 0ull;
-      }
-    }
+  for (int c0 = 0; c0 < nchunks; c0 += kWave) {
+    if (c0 > 0) load(c0 + lane);
     wave_topk<E>(kv, rk, k, sm);
   }
   unpack(rk, rv, ri);
