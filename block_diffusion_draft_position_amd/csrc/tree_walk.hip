@@ -39,7 +39,12 @@ __device__ __forceinline__ int unpack_id(unsigned long long key) {
   return (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
 }
 
-__global__ void __launch_bounds__(kMaxWaves * kWave)
+// ONE: the row is a single batch, so the scan is on the latency path and takes the
+// batch maximum first (a short dependent chain); longer rows are streamed, and there
+// the compare-as-you-go scan keeps up with the loads better (measured).  Two workgroups
+// per CU (8 waves per SIMD, at most 64 VGPRs): the row loads of one hide the other's scan.
+template <bool ONE>
+__global__ void __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
 tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ parent,
                  const int32_t* __restrict__ num_nodes, const float* __restrict__ target, int N,
                  int L, int vocab, int nbatch, bool vec_ok, unsigned long long* __restrict__ best,
@@ -77,12 +82,30 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
         for (int q = 0; q < 4; ++q) v[4 * b + q] = base + q < vocab ? x[base + q] : -INFINITY;
       }
     }
+    if constexpr (ONE) {
+      // the batch's maximum first, then the first element that holds it: elements are
+      // visited in increasing id order, so ties go to the smaller id
+      float mb = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      const int i = lo + ((e / 4) * kWave + lane) * 4 + e % 4;
-      if (i < vocab && better(v[e], i, bv, bi)) {
-        bv = v[e];
-        bi = i;
+      for (int e = 0; e < kE; ++e) mb = fmaxf(mb, v[e]);
+      int ib = INT_MAX;
+#pragma unroll
+      for (int e = kE - 1; e >= 0; --e) {
+        const int i = lo + ((e / 4) * kWave + lane) * 4 + e % 4;
+        if (v[e] == mb && i < vocab) ib = i;
+      }
+      if (ib != INT_MAX && better(mb, ib, bv, bi)) {
+        bv = mb;
+        bi = ib;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        const int i = lo + ((e / 4) * kWave + lane) * 4 + e % 4;
+        if (i < vocab && better(v[e], i, bv, bi)) {
+          bv = v[e];
+          bi = i;
+        }
       }
     }
   }
@@ -165,10 +188,16 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
   unsigned long long* best =
       reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + plan.counter_bytes);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0);
-  hipLaunchKernelGGL(tree_walk_kernel, dim3((unsigned)((int64_t)S * N)), dim3(plan.waves * kWave),
-                     3 * sizeof(int) * N, st, tree_tok, parent, num_nodes, target, N, L,
-                     (int)vocab, plan.nbatch, vec_ok, best, counters, accept_len, acc_nodes,
-                     acc_tok, bonus_out);
+  const dim3 grid((unsigned)((int64_t)S * N)), block(plan.waves * kWave);
+  const size_t smem = 3 * sizeof(int) * N;
+  if (plan.nbatch == 1)
+    hipLaunchKernelGGL(tree_walk_kernel<true>, grid, block, smem, st, tree_tok, parent, num_nodes,
+                       target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, accept_len,
+                       acc_nodes, acc_tok, bonus_out);
+  else
+    hipLaunchKernelGGL(tree_walk_kernel<false>, grid, block, smem, st, tree_tok, parent, num_nodes,
+                       target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, accept_len,
+                       acc_nodes, acc_tok, bonus_out);
   return hipGetLastError();
 }
 
