@@ -196,10 +196,11 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
 
 // walk
 struct WalkPlan {
-  int waves;             // waves per workgroup (one workgroup per node row)
-  int nbatch;            // batches of waves * 64 * 32 logits per row
+  int waves;             // waves per workgroup
+  int nbatch;            // batches of waves * 64 * 32 logits per row: one workgroup each
   size_t counter_bytes;  // per-sequence completion counters at the front of the workspace
-  size_t ws_bytes;       // counters + one 64-bit arg-max key per node
+  size_t rowcnt_bytes;   // then per-row counters of finished batches
+  size_t ws_bytes;       // counters + row counters + one 64-bit arg-max key per node
 };
 WalkPlan walk_plan(int S, int B, int64_t vocab);
 hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,

@@ -2,16 +2,19 @@
 // the target's decoding rule from the root, accept while its token matches a child,
 // carry the first mismatch as the next bonus token).
 //
-// One kernel.  A workgroup of up to 16 waves takes one node's row of target logits,
-// read in batches of 16-byte loads issued together, and finds its arg-max: larger
-// value first, equal values by smaller id.  The winner is stored as the node's
-// 64-bit key in the workspace (the order-preserving image of the value above the
-// complement of the id).  Padding nodes (past num_nodes) are skipped.  Each
-// workgroup then bumps its sequence's counter; the one that completes the sequence
-// reads the node keys, clears the counter for the next call, and walks the tree
-// with one wave.  Keys and counters pass between workgroups through device-scope
-// atomics only: the key store is a returning exchange, whose result is awaited
-// before the counter increment, so no cache-wide fence is needed.
+// One kernel.  A workgroup of up to 16 waves takes one batch (16 waves x 64 lanes x 32
+// logits) of one node's row of target logits, loaded with 16-byte loads issued
+// together, and finds its arg-max: larger value first, equal values by smaller id.
+// Rows longer than a batch are split over several workgroups, so a grid of a few
+// hundred rows has no row left over for a lone second round.  The winner enters the
+// node's 64-bit key in the workspace (the order-preserving image of the value above
+// the complement of the id) by a returning atomic maximum; a per-row counter finds
+// the row's last batch, which bumps the sequence's counter; the workgroup that
+// completes the sequence reads the node keys, clears keys and counters for the next
+// call, and walks the tree with one wave.  Padding nodes (past num_nodes) are
+// skipped.  Keys and counters pass between workgroups through device-scope atomics
+// only: each atomic's result is awaited before the next is issued, so no cache-wide
+// fence is needed.
 #include <limits.h>
 
 #include "ddt_internal.h"
@@ -47,14 +50,16 @@ template <bool ONE>
 __global__ void __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
 tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ parent,
                  const int32_t* __restrict__ num_nodes, const float* __restrict__ target, int N,
-                 int L, int vocab, int nbatch, bool vec_ok, unsigned long long* __restrict__ best,
-                 unsigned* __restrict__ counters, int32_t* __restrict__ accept_len,
+                 int L, int vocab, int nseg, bool vec_ok, unsigned long long* __restrict__ best,
+                 unsigned* __restrict__ counters, unsigned* __restrict__ rowcnt,
+                 int32_t* __restrict__ accept_len,
                  int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
                  int32_t* __restrict__ bonus_out) {
   __shared__ unsigned long long red[kMaxWaves];
   __shared__ int last;
   extern __shared__ int smem[];
-  const int64_t row = blockIdx.x;  // s * N + n
+  const int64_t row = blockIdx.x / (unsigned)nseg;  // s * N + n
+  const int seg = (int)(blockIdx.x % (unsigned)nseg);  // the row's batch this workgroup scans
   const int s = (int)(row / N);
   const int n = (int)(row % N);
   const int nn = num_nodes[s];
@@ -67,8 +72,8 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
 
   float bv = -INFINITY;
   int bi = INT_MAX;
-  for (int bt = 0; bt < nbatch; ++bt) {
-    const int lo = (bt * nw + wave) * kWave * kE;
+  {
+    const int lo = (seg * nw + wave) * kWave * kE;
     float v[kE];
 #pragma unroll
     for (int b = 0; b < kE / 4; ++b) {
@@ -115,10 +120,23 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   if (tid == 0) {
     unsigned long long k = red[0];
     for (int w = 1; w < nw; ++w) k = red[w] > k ? red[w] : k;
-    const unsigned long long old = atomicExch(&best[row], k);
-    asm volatile("" ::"v"((unsigned)old) : "memory");  // the exchange has been performed
-    const unsigned prev = atomicAdd(&counters[s], 1u);
-    last = prev == (unsigned)nn - 1u;
+    // the row's key is the maximum over its segments; the counters count finished
+    // segments per row and finished rows per sequence.  Each atomic's result is
+    // awaited before the next one is issued, which orders them without a fence.
+    const unsigned long long old = atomicMax(&best[row], k);
+    asm volatile("" ::"v"((unsigned)old) : "memory");  // the maximum has been performed
+    bool row_done = true;
+    if (nseg > 1) {
+      const unsigned pr = atomicAdd(&rowcnt[row], 1u);
+      asm volatile("" ::"v"(pr) : "memory");
+      row_done = pr == (unsigned)nseg - 1u;
+      if (row_done) __hip_atomic_store(&rowcnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    last = false;
+    if (row_done) {
+      const unsigned prev = atomicAdd(&counters[s], 1u);
+      last = prev == (unsigned)nn - 1u;
+    }
   }
   __syncthreads();
   if (!last) return;
@@ -130,6 +148,8 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   for (int i = tid; i < nn; i += blockDim.x) {
     const unsigned long long k =
         __hip_atomic_load(best + (int64_t)s * N + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // cleared for the next call, whose maxima start from 0
+    __hip_atomic_store(best + (int64_t)s * N + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     want[i] = unpack_id(k);
     tok[i] = tree_tok[(int64_t)s * N + i];
     par[i] = parent[(int64_t)s * N + i];
@@ -172,9 +192,12 @@ WalkPlan walk_plan(int S, int B, int64_t vocab) {
   WalkPlan p;
   const int64_t rows = (int64_t)S * (B + 1);
   p.waves = (int)std::min<int64_t>(kMaxWaves, ceil_div(vocab, (int64_t)kWave * kE));
+  // one batch of waves * 64 * kE logits per workgroup: a long row is split over several
+  // workgroups, so no row makes a lone extra round of the grid
   p.nbatch = (int)ceil_div(vocab, (int64_t)p.waves * kWave * kE);
   p.counter_bytes = align_up((size_t)S * sizeof(unsigned), 256);
-  p.ws_bytes = p.counter_bytes + align_up((size_t)rows * sizeof(unsigned long long), 256);
+  p.rowcnt_bytes = align_up((size_t)rows * sizeof(unsigned), 256);
+  p.ws_bytes = p.counter_bytes + p.rowcnt_bytes + align_up((size_t)rows * sizeof(unsigned long long), 256);
   return p;
 }
 
@@ -185,19 +208,20 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             hipStream_t st) {
   const int N = B + 1;
   unsigned* counters = static_cast<unsigned*>(ws);
-  unsigned long long* best =
-      reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + plan.counter_bytes);
+  unsigned* rowcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + plan.counter_bytes);
+  unsigned long long* best = reinterpret_cast<unsigned long long*>(
+      static_cast<char*>(ws) + plan.counter_bytes + plan.rowcnt_bytes);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0);
-  const dim3 grid((unsigned)((int64_t)S * N)), block(plan.waves * kWave);
+  const dim3 grid((unsigned)((int64_t)S * N * plan.nbatch)), block(plan.waves * kWave);
   const size_t smem = 3 * sizeof(int) * N;
   if (plan.nbatch == 1)
     hipLaunchKernelGGL(tree_walk_kernel<true>, grid, block, smem, st, tree_tok, parent, num_nodes,
-                       target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, accept_len,
-                       acc_nodes, acc_tok, bonus_out);
+                       target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, rowcnt,
+                       accept_len, acc_nodes, acc_tok, bonus_out);
   else
     hipLaunchKernelGGL(tree_walk_kernel<false>, grid, block, smem, st, tree_tok, parent, num_nodes,
-                       target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, accept_len,
-                       acc_nodes, acc_tok, bonus_out);
+                       target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, rowcnt,
+                       accept_len, acc_nodes, acc_tok, bonus_out);
   return hipGetLastError();
 }
 

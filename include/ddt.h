@@ -215,7 +215,10 @@ int ddt_tree_attention(const void* q, const void* k_cache, const void* v_cache,
  * acc_nodes  [S, L]  accepted node indices in order, -1 padded.
  * acc_tok    [S, L]  their tokens, -1 padded.
  * bonus_out  [S]     the target's token at the last accepted node.
- * ws        at least ddt_tree_walk_workspace_size(S, B, vocab) bytes.
+ * ws        at least ddt_tree_walk_workspace_size(S, B, vocab) bytes of device memory,
+ *           zero-filled before its first use; every call leaves it zero-filled again
+ *           (completion counters and arg-max keys).  Calls that share a workspace
+ *           must not overlap.
  * Errors: null pointer; S < 1; L outside [1, DDT_MAX_L]; B outside [0, DDT_MAX_B];
  *         vocab < 1 or > INT32_MAX; ws too small.
  */
