@@ -220,7 +220,9 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
       cnt[j] = above(j, tau);
       mine += cnt[j];
     }
-    int total = wave_sum_i(mine);
+    // uniform across the wave: the compiler then keeps the counts, the budget and the
+    // search prefixes below in scalar registers and branches on them without masks
+    int total = __builtin_amdgcn_readfirstlane(wave_sum_i(mine));
 
     if (total == 0) {
       // nothing clears tau: take the single best head, the lowest node on ties
@@ -279,9 +281,10 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
           unsigned long long t = 0ull;
           for (int b = 62; b >= 0; b -= 2) {
             const unsigned long long c1 = t | (1ull << b), c2 = t | (2ull << b), c3 = t | (3ull << b);
-            const int n1 = __popcll(ballot(has && mk >= c1));
-            const int n2 = __popcll(ballot(has && mk >= c2));
-            const int n3 = __popcll(ballot(has && mk >= c3));
+            // mk = 0 where no candidate, below every threshold
+            const int n1 = __popcll(ballot(mk >= c1));
+            const int n2 = __popcll(ballot(mk >= c2));
+            const int n3 = __popcll(ballot(mk >= c3));
             int nb = R + 1;
             if (n3 >= R) {
               t = c3;

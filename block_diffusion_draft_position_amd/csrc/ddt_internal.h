@@ -19,7 +19,7 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-__device__ __forceinline__ unsigned long long ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ unsigned long long ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 template <typename T>
 __device__ __forceinline__ T readlane(T v, int lane) {
