@@ -149,17 +149,18 @@ __device__ void rank_select(Valid valid, Cand cand, KeyOf keyof, bool carry,
     rk = lane < min(C, K) ? sm.ok[lane] : 0ull;
     wave_lds_sync();  // sm is free again
   } else {
-    unsigned long long taken = 0ull;  // bit e: element e taken; bit E: the carried key
+    unsigned long long taken = 0ull;  // bit e: element e taken
+    bool carry_taken = false;         // the carried key taken
     unsigned long long out = 0ull;
     for (int r = 0; r < K; ++r) {
-      unsigned long long b = ((taken >> E) & 1ull) ? 0ull : rk;
+      unsigned long long b = carry_taken ? 0ull : rk;
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if (valid(e) && !((taken >> e) & 1ull) && keyof(e) > b) b = keyof(e);
       const unsigned long long w = wave_max_u64(b);
       if (w == 0ull) break;  // nothing left anywhere
       if (b == w) {
-        if (rk == w && !((taken >> E) & 1ull)) taken |= 1ull << E;
+        if (rk == w) carry_taken = true;
 #pragma unroll
         for (int e = 0; e < E; ++e)
           if (valid(e) && keyof(e) == w) taken |= 1ull << e;
