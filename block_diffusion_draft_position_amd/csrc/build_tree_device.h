@@ -12,10 +12,11 @@ namespace ddt {
 namespace tree {
 
 constexpr int kRankCap = 256;  // final rounds with at most this many candidates rank them exactly
+constexpr int kGatherCap = 2048;  // radix selects over at most this many keys read them from LDS
 constexpr unsigned long long kIdxMask = 0x3ffull;  // low key bits that carry the node-order number
 
 struct TreeSmem {
-  unsigned long long* key;  // [kRankCap] final-round candidate keys
+  unsigned long long* key;  // [kGatherCap] final-round candidate keys
   int* sel;                 // [kRankCap] candidate taken?
   double* score;  // [N] node -> prefix log-probability
   float* lq;      // [L*K]
@@ -32,7 +33,7 @@ struct TreeSmem {
 };
 
 __host__ __device__ constexpr size_t smem_bytes(int N, int LK) {
-  return (sizeof(unsigned long long) + sizeof(int)) * kRankCap + sizeof(double) * (size_t)N +
+  return sizeof(unsigned long long) * kGatherCap + sizeof(int) * kRankCap + sizeof(double) * (size_t)N +
          (sizeof(float) + sizeof(int)) * (size_t)LK + sizeof(int) * 256 + sizeof(int) * 8 * (size_t)N;
 }
 
@@ -97,7 +98,7 @@ __device__ __forceinline__ unsigned long long key_of(double x) {
 __device__ inline TreeSmem carve(unsigned char* p, int N, int LK) {
   TreeSmem sm;
   sm.key = reinterpret_cast<unsigned long long*>(p);
-  p += sizeof(unsigned long long) * kRankCap;
+  p += sizeof(unsigned long long) * kGatherCap;
   sm.score = reinterpret_cast<double*>(p);
   p += sizeof(double) * N;
   sm.sel = reinterpret_cast<int*>(p);
@@ -194,6 +195,8 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
   int n = 1;  // nodes selected so far, root included
   while (n - 1 < B) {
     const int R = B - (n - 1);
+    // slots that hold nodes (and so streams): per-slot work and wave scans stop there
+    const int jn = (n + kWave - 1) / kWave;
     if constexpr (SK > 0) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
@@ -207,7 +210,7 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
     double tl = -INFINITY;
 #pragma unroll
     for (int j = 0; j < J; ++j)
-      if (cur[j] < K) {
+      if (j < jn && cur[j] < K) {
         live = true;
         tl = fmax(tl, head[j] + (double)nxt[j]);
       }
@@ -217,7 +220,7 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
     int mine = 0;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      cnt[j] = above(j, tau);
+      cnt[j] = j < jn ? above(j, tau) : 0;
       mine += cnt[j];
     }
     // uniform across the wave: the compiler then keeps the counts, the budget and the
@@ -246,9 +249,12 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
         int base = 0;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-          const int incl = wave_scan(cnt[j]);
-          off[j] = base + incl - cnt[j];
-          base += readlane(incl, kWave - 1);
+          off[j] = base;
+          if (j < jn) {
+            const int incl = wave_scan(cnt[j]);
+            off[j] = base + incl - cnt[j];
+            base += readlane(incl, kWave - 1);
+          }
         }
       }
       // Candidate keys: the score's order-preserving 64 bits with the lowest ten replaced
@@ -364,18 +370,38 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
         unsigned long long pmask = top >= 63 ? 0ull : (~0ull << (top + 1));
         unsigned long long prefix = kmax & pmask;
         int k = R;
+        // Up to kGatherCap candidates: their keys are formed once, in node order, and
+        // every pass reads them from LDS with all lanes; beyond, each pass recomputes
+        // them stream by stream.
+        const bool gathered = total <= kGatherCap;
+        if (gathered) {
+#pragma unroll
+          for (int j = 0; j < J; ++j)
+            if (j < jn) {
+#pragma unroll 4
+              for (int i = 0; i < cnt[j]; ++i) sm.key[off[j] + i] = key_of(sc[j] + lq(dep[j], cur[j] + i));
+            }
+        }
         for (int hi = top; hi >= 0; hi -= 8) {
           const int lo = max(hi - 7, 0);
           const int nbins = 1 << (hi - lo + 1);
           const unsigned long long dmask = (unsigned long long)(nbins - 1);
           for (int b = lane; b < 256; b += kWave) sm.hist[b] = 0;
           sync();
-#pragma unroll
-          for (int j = 0; j < J; ++j)
-            for (int i = 0; i < cnt[j]; ++i) {
-              const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i));
+          if (gathered) {
+#pragma unroll 4
+            for (int f = lane; f < total; f += kWave) {
+              const unsigned long long key = sm.key[f];
               if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> lo) & dmask], 1);
             }
+          } else {
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+              for (int i = 0; i < cnt[j]; ++i) {
+                const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i));
+                if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> lo) & dmask], 1);
+              }
+          }
           sync();
           // lane l holds bins nbins-1-4l .. nbins-4-4l: the scan runs from the top bin down
           int h[4], loc = 0;
@@ -417,8 +443,10 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
         for (int j = 0; j < J; ++j) {
           gt[j] = 0;
           eq[j] = 0;
-          for (int i = 0; i < cnt[j]; ++i) {
-            const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i)) & pmask;
+#pragma unroll 4
+          for (int i = 0; i < (j < jn ? cnt[j] : 0); ++i) {
+            const unsigned long long key =
+                (gathered ? sm.key[off[j] + i] : key_of(sc[j] + lq(dep[j], cur[j] + i))) & pmask;
             gt[j] += key > prefix;
             eq[j] += key == prefix;
           }
@@ -426,10 +454,13 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
         int before = 0;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-          const int incl = wave_scan(eq[j]);
-          const int take = min(max(k - (before + incl - eq[j]), 0), eq[j]);
-          cnt[j] = gt[j] + take;
-          before += readlane(incl, kWave - 1);
+          cnt[j] = 0;
+          if (j < jn) {
+            const int incl = wave_scan(eq[j]);
+            const int take = min(max(k - (before + incl - eq[j]), 0), eq[j]);
+            cnt[j] = gt[j] + take;
+            before += readlane(incl, kWave - 1);
+          }
         }
       }
       total = R;
@@ -441,49 +472,53 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
     int base = n;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int incl = wave_scan(cnt[j]);
-      const int firstid = base + incl - cnt[j];
-      const int u = j * kWave + lane;
-      if (cnt[j] > 0) {
-        for (int i = 0; i < cnt[j]; ++i) {
-          const int x = firstid + i;
-          if (x < N) {
-            sm.parent[x] = u;
-            sm.rank[x] = cur[j] + i;
+      if (j < jn) {  // no streams past jn, so no candidates
+        const int incl = wave_scan(cnt[j]);
+        const int firstid = base + incl - cnt[j];
+        const int u = j * kWave + lane;
+        if (cnt[j] > 0) {
+          for (int i = 0; i < cnt[j]; ++i) {
+            const int x = firstid + i;
+            if (x < N) {
+              sm.parent[x] = u;
+              sm.rank[x] = cur[j] + i;
+            }
           }
-        }
-        const int cn = cur[j] + cnt[j];
-        if constexpr (SK > 0) {
-          float hv = -INFINITY;
+          const int cn = cur[j] + cnt[j];
+          if constexpr (SK > 0) {
+            float hv = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < KW; ++r)
-            if (r == cn) hv = rowv[j][r];
-          head[j] = cn < K ? sc[j] + (double)hv : -INFINITY;
-        } else {
-          head[j] = cn < K ? sc[j] + lq(dep[j], cn) : -INFINITY;
+            for (int r = 0; r < KW; ++r)
+              if (r == cn) hv = rowv[j][r];
+            head[j] = cn < K ? sc[j] + (double)hv : -INFINITY;
+          } else {
+            head[j] = cn < K ? sc[j] + lq(dep[j], cn) : -INFINITY;
+          }
+          cur[j] = cn;
         }
-        cur[j] = cn;
+        base += readlane(incl, kWave - 1);
       }
-      base += readlane(incl, kWave - 1);
     }
     sync();
     // each new node opens its stream
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int x = j * kWave + lane;
-      if (x >= n && x < n + total) {
-        const int u = sm.parent[x];
-        const int r = sm.rank[x];
-        const int pd = sm.depth[u];
-        const double ps = sm.score[u];
-        dep[j] = pd + 1;
-        sc[j] = ps + lq(pd, r);
-        const bool open = dep[j] < L;
-        cur[j] = open ? 0 : K;
-        head[j] = open ? sc[j] + lq(dep[j], 0) : -INFINITY;
-        nxt[j] = dep[j] + 1 < L ? sm.lq[(dep[j] + 1) * K] : -INFINITY;
-        sm.depth[x] = dep[j];
-        sm.score[x] = sc[j];
+      if (j * kWave < n + total) {
+        const int x = j * kWave + lane;
+        if (x >= n && x < n + total) {
+          const int u = sm.parent[x];
+          const int r = sm.rank[x];
+          const int pd = sm.depth[u];
+          const double ps = sm.score[u];
+          dep[j] = pd + 1;
+          sc[j] = ps + lq(pd, r);
+          const bool open = dep[j] < L;
+          cur[j] = open ? 0 : K;
+          head[j] = open ? sc[j] + lq(dep[j], 0) : -INFINITY;
+          nxt[j] = dep[j] + 1 < L ? sm.lq[(dep[j] + 1) * K] : -INFINITY;
+          sm.depth[x] = dep[j];
+          sm.score[x] = sc[j];
+        }
       }
     }
     n += total;
@@ -528,7 +563,7 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int x = j * kWave + lane;
-      if (x < n && x > 0 && dep[j] == d) {
+      if (j * kWave < n && x < n && x > 0 && dep[j] == d) {
         const int ci = sm.first[par[j]] + rnk[j];
         cn[j] = ci;
         if (ci >= 0 && ci < N) {
