@@ -198,6 +198,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
 struct WalkPlan {
   int waves;             // waves per workgroup
   int nbatch;            // batches of waves * 64 * 32 logits per row: one workgroup each
+  bool short_scan;       // the grid fits the CUs at once: latency-path scan
   size_t counter_bytes;  // per-sequence completion counters at the front of the workspace
   size_t rowcnt_bytes;   // then per-row counters of finished batches
   size_t ws_bytes;       // counters + row counters + one 64-bit arg-max key per node

@@ -2,11 +2,12 @@
 // the target's decoding rule from the root, accept while its token matches a child,
 // carry the first mismatch as the next bonus token).
 //
-// One kernel.  A workgroup takes one batch of one node's row of target logits (up to 16
-// waves x 64 lanes x 32 logits for a row that fits one batch, 8 waves otherwise),
-// loaded with 16-byte loads issued together, and finds its arg-max: larger value
-// first, equal values by smaller id.  Longer rows are split over several workgroups,
-// so a grid of a few hundred rows has no row left over for a lone second round.  The winner enters the
+// One kernel.  A workgroup takes one batch of one node's row of target logits (waves x
+// 64 lanes x 32 logits: 16 waves for a row that fits one batch, 8 otherwise, 4 when the
+// grid would leave most CUs idle), loaded with 16-byte loads issued together, and finds
+// its arg-max: larger value first, equal values by smaller id.  Longer rows are split
+// over several workgroups, so a grid of a few hundred rows has no row left over for a
+// lone second round.  The winner enters the
 // node's 64-bit key in the workspace (the order-preserving image of the value above
 // the complement of the id) by a returning atomic maximum; a per-row counter finds
 // the row's last batch, which bumps the sequence's counter; the workgroup that
@@ -42,9 +43,9 @@ __device__ __forceinline__ int unpack_id(unsigned long long key) {
   return (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
 }
 
-// ONE: the row is a single batch, so the scan is on the latency path and takes the
-// batch maximum first (a short dependent chain); longer rows are streamed, and there
-// the compare-as-you-go scan keeps up with the loads better (measured).  Two workgroups
+// ONE: the whole grid runs at once, so the scan is on the latency path and takes the
+// batch maximum first (a short dependent chain); when workgroups stream in rounds, the
+// compare-as-you-go scan keeps up with the loads better (measured).  Two workgroups
 // per CU (8 waves per SIMD, at most 64 VGPRs): the row loads of one hide the other's scan.
 template <bool ONE>
 __global__ void __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
@@ -194,10 +195,16 @@ WalkPlan walk_plan(int S, int B, int64_t vocab) {
   // A row that fits one batch of 16 waves is one workgroup; longer rows are split into
   // batches of 8 waves (8 * 64 * kE logits), one workgroup each, so no row makes a lone
   // extra round of the grid (8-wave batches measured 5-6% faster than 16 on C2 and C3).
+  // A grid of fewer workgroups than half the CUs splits its rows further, down to
+  // 4-wave batches, so that more CUs stream the logits (C1, cold caches: 13.0 -> 11.6
+  // us per call).
   const int64_t per_wave = (int64_t)kWave * kE;
-  p.waves = (int)std::min<int64_t>(vocab <= kMaxWaves * per_wave ? kMaxWaves : kMaxWaves / 2,
-                                   ceil_div(vocab, per_wave));
+  int w = vocab <= kMaxWaves * per_wave ? kMaxWaves : kMaxWaves / 2;
+  while (w > 4 && rows * ceil_div(vocab, (int64_t)w * per_wave) < cu_count() / 2) w /= 2;
+  p.waves = (int)std::min<int64_t>(w, ceil_div(vocab, per_wave));
   p.nbatch = (int)ceil_div(vocab, (int64_t)p.waves * per_wave);
+  // the whole grid at once on the CUs: the scan is on the latency path
+  p.short_scan = rows * p.nbatch <= cu_count();
   p.counter_bytes = align_up((size_t)S * sizeof(unsigned), 256);
   p.rowcnt_bytes = align_up((size_t)rows * sizeof(unsigned), 256);
   p.ws_bytes = p.counter_bytes + p.rowcnt_bytes + align_up((size_t)rows * sizeof(unsigned long long), 256);
@@ -217,7 +224,7 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0);
   const dim3 grid((unsigned)((int64_t)S * N * plan.nbatch)), block(plan.waves * kWave);
   const size_t smem = 3 * sizeof(int) * N;
-  if (plan.nbatch == 1)
+  if (plan.short_scan)
     hipLaunchKernelGGL(tree_walk_kernel<true>, grid, block, smem, st, tree_tok, parent, num_nodes,
                        target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, rowcnt,
                        accept_len, acc_nodes, acc_tok, bonus_out);
