@@ -443,12 +443,32 @@ __device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
         for (int j = 0; j < J; ++j) {
           gt[j] = 0;
           eq[j] = 0;
-#pragma unroll 4
-          for (int i = 0; i < (j < jn ? cnt[j] : 0); ++i) {
-            const unsigned long long key =
-                (gathered ? sm.key[off[j] + i] : key_of(sc[j] + lq(dep[j], cur[j] + i))) & pmask;
-            gt[j] += key > prefix;
-            eq[j] += key == prefix;
+          if (j >= jn) continue;
+          if (gathered) {
+            // a stream's keys are sorted (largest first), so both counts are searches:
+            // the first key at or below the prefix, and the first key below it
+            auto first = [&](bool strict) {
+              int lo = 0, len = cnt[j];
+              while (len > 0) {
+                const int half = len >> 1;
+                const unsigned long long key = sm.key[off[j] + lo + half] & pmask;
+                if (strict ? key > prefix : key >= prefix) {
+                  lo += half + 1;
+                  len -= half + 1;
+                } else {
+                  len = half;
+                }
+              }
+              return lo;
+            };
+            gt[j] = first(true);
+            eq[j] = first(false) - gt[j];
+          } else {
+            for (int i = 0; i < cnt[j]; ++i) {
+              const unsigned long long key = key_of(sc[j] + lq(dep[j], cur[j] + i)) & pmask;
+              gt[j] += key > prefix;
+              eq[j] += key == prefix;
+            }
           }
         }
         int before = 0;
