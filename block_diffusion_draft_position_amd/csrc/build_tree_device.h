@@ -129,7 +129,7 @@ __device__ inline TreeSmem carve(unsigned char* p, int N, int LK) {
 // each stream's logq row in SK registers for the round, so its reads are issued
 // together and the per-rank loops run SK steps.
 template <int J, int SK, typename Sync>
-__device__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
+__device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
                      int32_t* __restrict__ tree_tok, int32_t* __restrict__ tree_parent,
                      int32_t* __restrict__ tree_depth, float* __restrict__ node_logq,
                      int32_t* __restrict__ pos_ids, int P, Sync sync) {
