@@ -236,6 +236,17 @@ def test_large_budget_multi_word_mask(fused):
     run_case(cfg, fused=fused)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
+def test_widest_round(fused):
+    """K = 64 and B = 1023 over three positions: the third round has 3369 candidates for
+    809 places, more than the 2048 whose keys the radix select keeps in LDS, so each of
+    its passes recomputes the keys stream by stream (the earlier rounds take 45 and 169
+    candidates: all of them, then a ranked cut)."""
+    cfg = configs.custom("widest", S=1, L=3, V=5000, K=64, B=1023, prefix=(64, 64), Hq=4, Hkv=1,
+                         D=64, dtype="bf16")
+    run_case(cfg, rows_per_seq=64, fused=fused)
+
+
 def test_fused_matches_calls_bitwise():
     """ddt_draft_tree equals ddt_topk -> ddt_build_tree -> ddt_tree_mask bit for bit,
     including the fp32 log-probabilities, on a long-vocabulary batch."""
