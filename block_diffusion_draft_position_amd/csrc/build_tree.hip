@@ -52,7 +52,7 @@ build_tree_kernel(const int32_t* __restrict__ topk_tok, const float* __restrict_
   const int64_t o = (int64_t)s * N;
   const int n = tree::build<J, SK>(sm, L, K, B, bonus_tok, tree_tok + o, tree_parent + o,
                                    tree_depth + o, node_logq ? node_logq + o : nullptr, nullptr,
-                                   0, [] { __syncthreads(); });
+                                   0, [] { __syncthreads(); }, [](int) {});  // the table is loaded
   if (lane == 0) num_nodes[s] = n;
 }
 

@@ -127,12 +127,15 @@ __device__ inline TreeSmem carve(unsigned char* p, int N, int LK) {
 // traffic: a workgroup barrier when the wave is alone, a wave barrier otherwise.
 // J register slots of streams per lane.  SK > 0 (K <= SK, SK = 8 or 16, J <= 2) caches
 // each stream's logq row in SK registers for the round, so its reads are issued
-// together and the per-rank loops run SK steps.
-template <int J, int SK, typename Sync>
+// together and the per-rank loops run SK steps.  rows(m) returns once rows 0 .. m-1
+// of sm.lq / sm.ltok are in place (the fused kernel merges them while this runs): the
+// root needs rows 0 and 1, and round r at most rows 0 .. r + 2, since every round
+// deepens the tree by at most one.
+template <int J, int SK, typename Sync, typename Rows>
 __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonus_tok,
                      int32_t* __restrict__ tree_tok, int32_t* __restrict__ tree_parent,
                      int32_t* __restrict__ tree_depth, float* __restrict__ node_logq,
-                     int32_t* __restrict__ pos_ids, int P, Sync sync) {
+                     int32_t* __restrict__ pos_ids, int P, Sync sync, Rows rows) {
   const int lane = lane_id();
   const int N = B + 1;
   auto lq = [&](int d, int r) -> double { return (double)sm.lq[d * K + r]; };
@@ -153,6 +156,7 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
     dep[j] = 0;
     cur[j] = K;
   }
+  rows(min(L, 2));
   if (lane == 0) {  // the root
     cur[0] = 0;
     head[0] = lq(0, 0);
@@ -193,7 +197,8 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
   };
 
   int n = 1;  // nodes selected so far, root included
-  while (n - 1 < B) {
+  for (int round = 0; n - 1 < B; ++round) {
+    rows(min(L, round + 3));
     const int R = B - (n - 1);
     // slots that hold nodes (and so streams): per-slot work and wave scans stop there
     const int jn = (n + kWave - 1) / kWave;

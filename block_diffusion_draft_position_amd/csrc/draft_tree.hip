@@ -3,11 +3,13 @@
 // selection under the node budget (核心創新; 運作流程 step 2; 理論基礎) and the
 // ancestor-only mask with position ids (核心創新; 運作流程 step 3).
 //
-// One workgroup per sequence.  Wave w merges the chunk lists of draft positions
-// w, w + NW, ... (topk::merge_row) straight into the tree builder's LDS table; wave 0
-// then selects and numbers the tree (tree::build, synchronising with wave barriers
-// while the other waves wait); finally every wave forms mask rows from the canonical
-// parent array the builder left in LDS (mask::rows).  The results are identical to
+// One workgroup per sequence.  Wave 0 merges draft position 0's chunk lists
+// (topk::merge_row) straight into the tree builder's LDS table, the other waves the
+// remaining positions, each row flagged in LDS once written.  Wave 0 then selects and
+// numbers the tree (tree::build, synchronising with wave barriers), waiting on a
+// row's flag only when a round first needs it, so the build overlaps the merges of
+// the deeper positions; finally every wave forms mask rows from the canonical parent
+// array the builder left in LDS (mask::rows).  The results are identical to
 // ddt_topk -> ddt_build_tree -> ddt_tree_mask; this path saves two launches and the
 // global round trips between them.
 #include "build_tree_device.h"
@@ -35,6 +37,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
   constexpr int NW = waves_for(J, ME);
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int nn_s;
+  __shared__ int ready[64];  // row i of the LDS table is written (L <= 64)
   const int s = blockIdx.x;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -47,7 +50,11 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
   const int bonus_tok = bonus[s];
   const int P = (pos_ids && cu_prefix) ? (int)(cu_prefix[s + 1] - cu_prefix[s]) : 0;
 
-  for (int i = wave; i < L; i += NW) {
+  if (threadIdx.x < 64) ready[threadIdx.x] = 0;
+  __syncthreads();
+  // wave 0 takes position 0 only, so that it reaches the build early; waves 1 .. NW-1
+  // take the others in turn
+  for (int i = wave; i < L; i = wave == 0 ? L : (i < NW ? NW + wave - 1 : i + NW - 1)) {
     const int64_t row = (int64_t)s * L + i;
     float rv;
     int ri;
@@ -60,14 +67,26 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
       if (topk_tok) topk_tok[row * K + lane] = ri;
       if (topk_logq) topk_logq[row * K + lane] = lqv;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the row, then its flag
+    if (lane == 0) __hip_atomic_store(&ready[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  __syncthreads();
   if (wave == 0) {
     const int64_t o = (int64_t)s * N;
     const int n = tree::build<J, SK>(sm, L, K, B, bonus_tok, tree_tok + o, tree_parent + o,
                                      tree_depth + o, node_logq ? node_logq + o : nullptr,
                                      (pos_ids && cu_prefix) ? pos_ids + o : nullptr, P,
-                                     [] { topk::wave_lds_sync(); });
+                                     [] { topk::wave_lds_sync(); },
+                                     [&](int m) {
+                                       for (;;) {
+                                         bool ok = true;
+                                         for (int i = lane; i < m; i += kWave)
+                                           ok &= __hip_atomic_load(&ready[i], __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+                                         if (!ballot(!ok)) break;
+                                         __builtin_amdgcn_s_sleep(1);
+                                       }
+                                       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                                     });
     if (lane == 0) {
       num_nodes[s] = n;
       nn_s = n;
