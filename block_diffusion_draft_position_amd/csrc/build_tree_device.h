@@ -220,7 +220,10 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
         tl = fmax(tl, head[j] + (double)nxt[j]);
       }
     if (!ballot(live)) break;  // the candidate tree is exhausted
-    const double tau = wave_max_d(tl);
+    // in the first round the root (lane 0, slot 0) holds the only stream, so the
+    // round's maximum and count are lane 0's own
+    const bool root_only = n == 1;
+    const double tau = root_only ? readlane_f64(tl, 0) : wave_max_d(tl);
     int cnt[J];
     int mine = 0;
 #pragma unroll
@@ -230,7 +233,7 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
     }
     // uniform across the wave: the compiler then keeps the counts, the budget and the
     // search prefixes below in scalar registers and branches on them without masks
-    int total = __builtin_amdgcn_readfirstlane(wave_sum_i(mine));
+    int total = __builtin_amdgcn_readfirstlane(root_only ? mine : wave_sum_i(mine));
 
     if (total == 0) {
       // nothing clears tau: take the single best head, the lowest node on ties
@@ -491,37 +494,61 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
       total = R;
     }
 
-    // the round's nodes get ids n .. n + total - 1 in (slot, lane) order.  A parent
-    // records only (parent, rank) for each new child; the child's own lane then reads
-    // its parent's depth and score and its logq row.
-    int base = n;
+    if (root_only) {
+      // the root's children ranks 0 .. total-1 become nodes 1 .. total, one per lane
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (j < jn) {  // no streams past jn, so no candidates
-        const int incl = wave_scan(cnt[j]);
-        const int firstid = base + incl - cnt[j];
-        const int u = j * kWave + lane;
-        if (cnt[j] > 0) {
-          for (int i = 0; i < cnt[j]; ++i) {
-            const int x = firstid + i;
-            if (x < N) {
-              sm.parent[x] = u;
-              sm.rank[x] = cur[j] + i;
-            }
-          }
-          const int cn = cur[j] + cnt[j];
-          if constexpr (SK > 0) {
-            float hv = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < KW; ++r)
-              if (r == cn) hv = rowv[j][r];
-            head[j] = cn < K ? sc[j] + (double)hv : -INFINITY;
-          } else {
-            head[j] = cn < K ? sc[j] + lq(dep[j], cn) : -INFINITY;
-          }
-          cur[j] = cn;
+      for (int j = 0; j < J; ++j) {
+        const int x = j * kWave + lane;
+        if (j * kWave <= total && x >= 1 && x <= total) {
+          sm.parent[x] = 0;
+          sm.rank[x] = x - 1;
         }
-        base += readlane(incl, kWave - 1);
+      }
+      if (lane == 0) {
+        if constexpr (SK > 0) {
+          float hv = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < KW; ++r)
+            if (r == total) hv = rowv[0][r];
+          head[0] = total < K ? (double)hv : -INFINITY;
+        } else {
+          head[0] = total < K ? lq(0, total) : -INFINITY;
+        }
+        cur[0] = total;
+      }
+    } else {
+      // the round's nodes get ids n .. n + total - 1 in (slot, lane) order.  A parent
+      // records only (parent, rank) for each new child; the child's own lane then reads
+      // its parent's depth and score and its logq row.
+      int base = n;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if (j < jn) {  // no streams past jn, so no candidates
+          const int incl = wave_scan(cnt[j]);
+          const int firstid = base + incl - cnt[j];
+          const int u = j * kWave + lane;
+          if (cnt[j] > 0) {
+            for (int i = 0; i < cnt[j]; ++i) {
+              const int x = firstid + i;
+              if (x < N) {
+                sm.parent[x] = u;
+                sm.rank[x] = cur[j] + i;
+              }
+            }
+            const int cn = cur[j] + cnt[j];
+            if constexpr (SK > 0) {
+              float hv = -INFINITY;
+#pragma unroll
+              for (int r = 0; r < KW; ++r)
+                if (r == cn) hv = rowv[j][r];
+              head[j] = cn < K ? sc[j] + (double)hv : -INFINITY;
+            } else {
+              head[j] = cn < K ? sc[j] + lq(dep[j], cn) : -INFINITY;
+            }
+            cur[j] = cn;
+          }
+          base += readlane(incl, kWave - 1);
+        }
       }
     }
     sync();
