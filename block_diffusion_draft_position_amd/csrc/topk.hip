@@ -97,16 +97,12 @@ topk_merge(int nchunks, int k, const unsigned long long* __restrict__ cand,
 
 TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   TopkPlan p;
-  // chunk length: short chunks (more waves) for small problems, long ones once the
-  // grid is full anyway
+  // chunk length: short chunks (more waves) for small problems, else 16 logits per
+  // lane.  32 per lane would halve the chunk lists to merge, but its 64-bit keys take
+  // 165 registers (two waves per SIMD instead of five), which measured slower: the
+  // draft side of C2 and C4 ran 5% and 11% faster with 16.
   const int64_t full = 4 * (int64_t)cu_count();
-  p.e = 32;
-  for (int e : {8, 16}) {
-    if (rows * ceil_div(vocab, (int64_t)kWave * e * 2) < full) {
-      p.e = e;
-      break;
-    }
-  }
+  p.e = rows * ceil_div(vocab, (int64_t)kWave * 8 * 2) < full ? 8 : 16;
   p.nchunks = (int)ceil_div(vocab, (int64_t)kWave * p.e);
   p.merge_e = k <= 8 ? 8 : k <= 32 ? 32 : 64;  // keys per lane: one chunk list each
   const size_t nslot = (size_t)rows * p.nchunks;
@@ -135,10 +131,8 @@ hipError_t launch_topk_partial(const float* logits, int64_t rows, int64_t vocab,
                      plan.nchunks, vec_ok, cand, stt)
   if (plan.e == 8)
     DDT_PART(8);
-  else if (plan.e == 16)
-    DDT_PART(16);
   else
-    DDT_PART(32);
+    DDT_PART(16);
 #undef DDT_PART
   return hipGetLastError();
 }
