@@ -37,7 +37,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
   constexpr int NW = waves_for(J, ME);
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int nn_s;
-  __shared__ int ready[64];  // row i of the LDS table is written (L <= 64)
+  __shared__ int ready[DDT_MAX_L];  // row i of the LDS table is written
   const int s = blockIdx.x;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -50,7 +50,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
   const int bonus_tok = bonus[s];
   const int P = (pos_ids && cu_prefix) ? (int)(cu_prefix[s + 1] - cu_prefix[s]) : 0;
 
-  if (threadIdx.x < 64) ready[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < DDT_MAX_L; i += NW * kWave) ready[i] = 0;
   __syncthreads();
   // wave 0 takes position 0 only, so that it reaches the build early; waves 1 .. NW-1
   // take the others in turn

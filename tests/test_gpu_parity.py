@@ -247,6 +247,15 @@ def test_widest_round(fused):
     run_case(cfg, rows_per_seq=64, fused=fused)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
+def test_size_limits(fused):
+    """L, K and B at the interface's limits (64, 64, 1023): the tree builder's LDS table
+    (about 90 KB) is above the default dynamic-LDS limit of a launch."""
+    cfg = configs.custom("limits", S=1, L=64, V=200, K=64, B=1023, prefix=(40, 40), Hq=2, Hkv=1,
+                         D=32, dtype="bf16")
+    run_case(cfg, fused=fused)
+
+
 def test_fused_matches_calls_bitwise():
     """ddt_draft_tree equals ddt_topk -> ddt_build_tree -> ddt_tree_mask bit for bit,
     including the fp32 log-probabilities, on a long-vocabulary batch."""
