@@ -12,7 +12,8 @@
 // the complement of the id) by a returning atomic maximum; a per-row counter finds
 // the row's last batch, which bumps the sequence's counter; the workgroup that
 // completes the sequence reads the node keys, clears keys and counters for the next
-// call, and walks the tree with one wave.  Padding nodes (past num_nodes) are
+// call, and walks the tree.  Only wave 0 of a workgroup goes past its LDS reduction:
+// the others leave at once instead of holding their slots through the atomics.  Padding nodes (past num_nodes) are
 // skipped.  Keys and counters pass between workgroups through device-scope atomics
 // only: each atomic's result is awaited before the next is issued, so no cache-wide
 // fence is needed.
@@ -57,7 +58,6 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
                  int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
                  int32_t* __restrict__ bonus_out) {
   __shared__ unsigned long long red[kMaxWaves];
-  __shared__ int last;
   extern __shared__ int smem[];
   const int64_t row = blockIdx.x / (unsigned)nseg;  // s * N + n
   const int seg = (int)(blockIdx.x % (unsigned)nseg);  // the row's batch this workgroup scans
@@ -118,7 +118,11 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   wave_argmax(bv, bi);
   if (lane == 0) red[wave] = bi == INT_MAX ? 0ull : pack(bv, bi);
   __syncthreads();
-  if (tid == 0) {
+  // wave 0 finishes the workgroup alone; the other waves free their slots now rather
+  // than waiting out the atomics' round trips
+  if (wave != 0) return;
+  bool last = false;
+  if (lane == 0) {
     unsigned long long k = red[0];
     for (int w = 1; w < nw; ++w) k = red[w] > k ? red[w] : k;
     // the row's key is the maximum over its segments; the counters count finished
@@ -133,20 +137,19 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
       row_done = pr == (unsigned)nseg - 1u;
       if (row_done) __hip_atomic_store(&rowcnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    last = false;
     if (row_done) {
       const unsigned prev = atomicAdd(&counters[s], 1u);
       last = prev == (unsigned)nn - 1u;
     }
   }
-  __syncthreads();
-  if (!last) return;
+  if (!__builtin_amdgcn_readfirstlane(last)) return;
 
-  // the sequence's last workgroup: collect the target's token at every node, walk
+  // the sequence's last workgroup (its wave 0): collect the target's token at every
+  // node, walk
   int* want = smem;         // [N] target's greedy token at each node
   int* tok = smem + N;      // [N]
   int* par = smem + 2 * N;  // [N]
-  for (int i = tid; i < nn; i += blockDim.x) {
+  for (int i = lane; i < nn; i += kWave) {
     const unsigned long long k =
         __hip_atomic_load(best + (int64_t)s * N + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // cleared for the next call, whose maxima start from 0
@@ -155,9 +158,11 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
     tok[i] = tree_tok[(int64_t)s * N + i];
     par[i] = parent[(int64_t)s * N + i];
   }
-  if (tid == 0) __hip_atomic_store(&counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (tid >= kWave) return;
+  if (lane == 0) __hip_atomic_store(&counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the wave's LDS writes above before its reads below
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int cur = 0;
   int a = 0;
   while (a < L) {
