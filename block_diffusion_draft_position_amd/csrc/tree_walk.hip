@@ -3,17 +3,17 @@
 // carry the first mismatch as the next bonus token).
 //
 // One kernel.  A workgroup takes one batch of one node's row of target logits (waves x
-// 64 lanes x 32 logits: 16 waves for a row that fits one batch, 8 otherwise, 4 when the
-// grid would leave most CUs idle), loaded with 16-byte loads issued together, and finds
-// its arg-max: larger value first, equal values by smaller id.  Longer rows are split
-// over several workgroups, so a grid of a few hundred rows has no row left over for a
-// lone second round.  The winner enters the
-// node's 64-bit key in the workspace (the order-preserving image of the value above
-// the complement of the id) by a returning atomic maximum; a per-row counter finds
-// the row's last batch, which bumps the sequence's counter; the workgroup that
-// completes the sequence reads the node keys, clears keys and counters for the next
-// call, and walks the tree.  Only wave 0 of a workgroup goes past its LDS reduction:
-// the others leave at once instead of holding their slots through the atomics.  Padding nodes (past num_nodes) are
+// 64 lanes x 32 logits: 16 waves for a row that fits one batch, 8 otherwise, down to
+// 2 when the grid would leave CUs idle), loaded with 16-byte loads issued together,
+// and finds its arg-max: larger value first, equal values by smaller id.  Longer rows
+// are split over several workgroups, so a grid of a few hundred rows has no row left
+// over for a lone second round.  The winner enters the node's 64-bit key in the
+// workspace (the order-preserving image of the value above the complement of the id)
+// by a returning atomic maximum; a per-row counter finds the row's last batch, which
+// bumps the sequence's counter; the workgroup that completes the sequence reads the
+// node keys, clears keys and counters for the next call, and walks the tree.  Only
+// wave 0 of a workgroup goes past its LDS reduction: the others leave at once instead
+// of holding their slots through the atomics.  Padding nodes (past num_nodes) are
 // skipped.  Keys and counters pass between workgroups through device-scope atomics
 // only: each atomic's result is awaited before the next is issued, so no cache-wide
 // fence is needed.
@@ -200,12 +200,12 @@ WalkPlan walk_plan(int S, int B, int64_t vocab) {
   // A row that fits one batch of 16 waves is one workgroup; longer rows are split into
   // batches of 8 waves (8 * 64 * kE logits), one workgroup each, so no row makes a lone
   // extra round of the grid (8-wave batches measured 5-6% faster than 16 on C2 and C3).
-  // A grid of fewer workgroups than half the CUs splits its rows further, down to
-  // 4-wave batches, so that more CUs stream the logits (C1, cold caches: 13.0 -> 11.6
-  // us per call).
+  // A grid of fewer workgroups than CUs splits its rows further, down to 2-wave
+  // batches, so that more CUs stream the logits (C1: 33 rows become 264 workgroups;
+  // 1% more rounds/s than 4-wave batches and 2.5% more than 16, paired runs).
   const int64_t per_wave = (int64_t)kWave * kE;
   int w = vocab <= kMaxWaves * per_wave ? kMaxWaves : kMaxWaves / 2;
-  while (w > 4 && rows * ceil_div(vocab, (int64_t)w * per_wave) < cu_count() / 2) w /= 2;
+  while (w > 2 && rows * ceil_div(vocab, (int64_t)w * per_wave) < cu_count()) w /= 2;
   p.waves = (int)std::min<int64_t>(w, ceil_div(vocab, per_wave));
   p.nbatch = (int)ceil_div(vocab, (int64_t)p.waves * per_wave);
   // the whole grid at once on the CUs: the scan is on the latency path
