@@ -945,11 +945,16 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_
     p.waves = (int)ceil_div(tiles, p.row_groups);
   }
   p.rows_pad = p.row_groups * p.waves * 32;
-  // prefix splits: about three (sequence, KV head, row group) units per CU (measured
-  // best on C2 and C3 shapes against two and four), and no split above 16K keys so
-  // that unequal prefix lengths still spread evenly
+  // prefix splits: about three (sequence, KV head, row group, split) units per CU
+  // (measured best on C2, C3 B >= 256 and C4 against one, two and four), and no split
+  // above 16K keys so that unequal prefix lengths still spread evenly.  With few
+  // (sequence, KV head, row group) units, up to a quarter of the CUs, three per CU cuts
+  // each unit into many splits of two to four tiles, whose partials outweigh the keys
+  // they cover; one per CU is then better (paired runs: C3 B = 16 to 128, +6-10%
+  // rounds/s).
   const int64_t units_base = (int64_t)S * Hkv * p.row_groups;
-  const int64_t target = (D == 128 ? 3 : 2) * (int64_t)cu_count();
+  const int64_t per_cu = D != 128 ? 2 : units_base * 4 <= cu_count() ? 1 : 3;
+  const int64_t target = per_cu * (int64_t)cu_count();
   const int64_t maxp = std::max<int64_t>(max_prefix, 0);
   const int64_t want = std::max<int64_t>(1, ceil_div(target, units_base));
   int64_t chunk = (int64_t)align_up((size_t)std::max<int64_t>(1, ceil_div(maxp, want)), kTile);
