@@ -93,7 +93,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
     }
   }
   __syncthreads();
-  mask::rows(sm.cpar, nn_s, N, W, mask + (int64_t)s * N * W, threadIdx.x, NW * kWave);
+  mask::rows(sm.cpar, nn_s, N, W, mask + (int64_t)s * N * W, threadIdx.x, NW * kWave, 0, N * W);
 }
 
 template <int J, int SK, int ME>

@@ -2,27 +2,35 @@
 // (DDTree page "策展 · X (Twitter)": section 核心創新 for the ancestor-only mask,
 // 運作流程 step 3 for compiling the tree into the target's inputs).
 //
-// One workgroup per sequence; the parent array is staged in LDS and the rows are
-// formed by mask::rows (tree_mask_device.h).
+// A sequence's N * W (node, word) items are cut into slices of kThreads * kPerThread,
+// one workgroup each; every workgroup stages the sequence's parent array in LDS and
+// forms its slice of the rows with mask::rows (tree_mask_device.h).  A deep tree's
+// items each walk up to L parent links, so the slices spread that over CUs (C3,
+// B = 512: 8721 items of a single sequence).
 #include "tree_mask_device.h"
 
 namespace ddt {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPerThread = 4;  // items per thread in a slice
 
 __global__ void __launch_bounds__(kThreads)
 tree_mask_kernel(const int32_t* __restrict__ parent, const int32_t* __restrict__ depth,
                  const int32_t* __restrict__ num_nodes, const int64_t* __restrict__ cu_prefix,
-                 int N, int W, uint32_t* __restrict__ mask, int32_t* __restrict__ pos_ids) {
+                 int N, int W, int slices, uint32_t* __restrict__ mask,
+                 int32_t* __restrict__ pos_ids) {
   extern __shared__ int par[];
-  const int s = blockIdx.x;
+  const int s = blockIdx.x / slices;
+  const int slice = blockIdx.x % slices;
   const int nn = num_nodes[s];
   const int32_t* pg = parent + (int64_t)s * N;
   for (int i = threadIdx.x; i < N; i += kThreads) par[i] = pg[i];
   __syncthreads();
-  mask::rows(par, nn, N, W, mask + (int64_t)s * N * W, threadIdx.x, kThreads);
-  if (pos_ids) {
+  const int per = kThreads * kPerThread;
+  mask::rows(par, nn, N, W, mask + (int64_t)s * N * W, threadIdx.x, kThreads, slice * per,
+             min(N * W, (slice + 1) * per));
+  if (pos_ids && slice == 0) {
     const int32_t P = (int32_t)(cu_prefix[s + 1] - cu_prefix[s]);
     for (int n = threadIdx.x; n < N; n += kThreads)
       pos_ids[(int64_t)s * N + n] = (n < nn) ? P + depth[(int64_t)s * N + n] : -1;
@@ -36,8 +44,9 @@ hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const i
                             int32_t* pos_ids, hipStream_t st) {
   const int N = B + 1;
   const int W = (N + 31) / 32;
-  hipLaunchKernelGGL(tree_mask_kernel, dim3(S), dim3(kThreads), sizeof(int) * N, st, parent, depth,
-                     num_nodes, cu_prefix, N, W, mask, cu_prefix ? pos_ids : nullptr);
+  const int slices = (int)ceil_div(N * W, kThreads * kPerThread);
+  hipLaunchKernelGGL(tree_mask_kernel, dim3(S * slices), dim3(kThreads), sizeof(int) * N, st, parent,
+                     depth, num_nodes, cu_prefix, N, W, slices, mask, cu_prefix ? pos_ids : nullptr);
   return hipGetLastError();
 }
 

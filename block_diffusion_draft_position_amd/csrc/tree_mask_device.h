@@ -8,14 +8,15 @@ namespace ddt {
 namespace mask {
 
 // Mask rows [N, W] of one sequence from its parent array in LDS (canonical order,
-// parents before children), by threads tid = 0 .. nthreads-1 of the caller.  A thread
-// owns one (node, word) item at a time and walks parent links from the node: parents
-// have smaller indices, so the walk passes the word's 32 node ids in one stretch and
-// stops below it.  Items are numbered row-major, so the stores of a wave are contiguous.
+// parents before children): items it0 .. it1-1 of the N * W (node, word) items, by
+// threads tid = 0 .. nthreads-1 of the caller.  A thread owns one item at a time and
+// walks parent links from the node: parents have smaller indices, so the walk passes
+// the word's 32 node ids in one stretch and stops below it.  Items are numbered
+// row-major, so the stores of a wave are contiguous.
 __device__ inline void rows(const int* __restrict__ par, int nn, int N, int W,
-                            uint32_t* __restrict__ mrow, int tid, int nthreads) {
-  const int items = N * W;
-  for (int it = tid; it < items; it += nthreads) {
+                            uint32_t* __restrict__ mrow, int tid, int nthreads, int it0,
+                            int it1) {
+  for (int it = it0 + tid; it < it1; it += nthreads) {
     const int n = it / W;
     const int w = it % W;
     uint32_t acc = 0u;
