@@ -13,7 +13,7 @@ namespace ddt {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = 4;  // items per thread in a slice
+constexpr int kPerThread = 1;  // items per thread in a slice (4: -0.75% rounds/s at C3, B = 512)
 
 __global__ void __launch_bounds__(kThreads)
 tree_mask_kernel(const int32_t* __restrict__ parent, const int32_t* __restrict__ depth,
