@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kMaxWaves = 16;  // waves per workgroup
 constexpr int kE = 32;         // logits per lane per batch
+constexpr int kGather = 6;     // node keys per lane loaded together by the walking wave
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -149,14 +150,31 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   int* want = smem;         // [N] target's greedy token at each node
   int* tok = smem + N;      // [N]
   int* par = smem + 2 * N;  // [N]
-  for (int i = lane; i < nn; i += kWave) {
-    const unsigned long long k =
-        __hip_atomic_load(best + (int64_t)s * N + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // cleared for the next call, whose maxima start from 0
-    __hip_atomic_store(best + (int64_t)s * N + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    want[i] = unpack_id(k);
-    tok[i] = tree_tok[(int64_t)s * N + i];
-    par[i] = parent[(int64_t)s * N + i];
+  // kGather nodes per lane have their loads in flight together: a load at a time made
+  // this gather a chain of round trips (C3, B = 512: 6 us for 513 nodes)
+  for (int i0 = 0; i0 < nn; i0 += kGather * kWave) {
+    unsigned long long k[kGather];
+    int t[kGather], p[kGather];
+#pragma unroll
+    for (int j = 0; j < kGather; ++j) {
+      const int i = i0 + j * kWave + lane;
+      if (i < nn) {
+        k[j] = __hip_atomic_load(best + (int64_t)s * N + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t[j] = tree_tok[(int64_t)s * N + i];
+        p[j] = parent[(int64_t)s * N + i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kGather; ++j) {
+      const int i = i0 + j * kWave + lane;
+      if (i < nn) {
+        // cleared for the next call, whose maxima start from 0
+        __hip_atomic_store(best + (int64_t)s * N + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        want[i] = unpack_id(k[j]);
+        tok[i] = t[j];
+        par[i] = p[j];
+      }
+    }
   }
   if (lane == 0) __hip_atomic_store(&counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // the wave's LDS writes above before its reads below
