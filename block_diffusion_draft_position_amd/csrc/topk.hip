@@ -10,7 +10,8 @@
 //                 into registers with 16-byte loads issued together (one memory
 //                 latency per chunk).  It forms the chunk's max and sum of
 //                 exp(x - max) (fp32 per lane, fp64 across the wave) and the chunk's
-//                 top-K list (wave_topk below), and writes both to the workspace:
+//                 top-K list (chunk_topk: wave_topk's selection with keys formed for
+//                 the candidates only), and writes both to the workspace:
 //                 the list as 64-bit keys, the statistics as a (max, sum) pair.
 //   topk_merge    one wave per row reads every chunk's list, one list per lane,
 //                 merges them with the same wave_topk, folds the statistics into the
@@ -51,25 +52,20 @@ topk_partial(const float* __restrict__ logits, int64_t stride, int vocab, int k,
       for (int q = 0; q < 4; ++q) v[4 * b + q] = base + q < vocab ? x[base + q] : -INFINITY;
     }
   }
-  auto idof = [&](int e) -> int {
-    const int i = lo + ((e / 4) * kWave + lane) * 4 + e % 4;
-    return i < vocab ? i : INT_MAX;
-  };
   // elements past the row's end hold -inf: they add nothing to the maximum or the sum
   float m = -INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
   const float M = wave_max(m);
+  // a chunk of masked (-inf) logits only sums to 0, not to exp(-inf - -inf) = NaN
+  const float Ms = M == -INFINITY ? 0.f : M;
   float se = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) se += __builtin_amdgcn_exp2f((v[e] - M) * kLog2e);
+  for (int e = 0; e < E; ++e) se += __builtin_amdgcn_exp2f((v[e] - Ms) * kLog2e);
   const double S = wave_sum((double)se);
 
-  unsigned long long key[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = pack(v[e], idof(e));  // 0 past the row's end
-  unsigned long long rk = 0ull;
-  wave_topk<E>(key, rk, k, sm);
+  unsigned long long rk;
+  chunk_topk<E>(v, x, lo, vocab, m, k, rk, sm);
   const int64_t slot = row * nchunks + c;
   if (lane < k) cand[slot * k + lane] = rk;
   if (lane == 0) stats[slot] = make_float2(M, (float)S);

@@ -49,6 +49,12 @@ __device__ __forceinline__ void unpack(unsigned long long key, float& v, int& id
   id = key ? (int)(0xffffffffu - (unsigned)(key & 0xffffffffull)) : INT_MAX;
 }
 
+// the value whose fkey is k, for k from a non-NaN value (-0 never occurs: fkey maps it
+// to +0's key, whose inverse is +0)
+__device__ __forceinline__ float unfkey(unsigned k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
   const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, lane);
   const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), lane);
@@ -107,6 +113,30 @@ __device__ __forceinline__ unsigned kth_upper(unsigned mh, int K) {
   return th;
 }
 
+// The C <= kCap candidate keys in sm.ck[0, C) (stored by this wave, not yet synced)
+// each count the keys above their own, which is their rank; on return lane i < K
+// holds the i-th largest in rk, other lanes 0.
+__device__ __forceinline__ void rank_count(int C, int K, unsigned long long& rk, WaveLds& sm) {
+  const int lane = lane_id();
+  const int Cp = (C + 1) & ~1;  // the counting loop reads two keys at a time
+  if (lane < Cp - C) sm.ck[C + lane] = 0ull;
+  wave_lds_sync();
+  for (int i0 = 0; i0 < C; i0 += kWave) {
+    const int i = i0 + lane;
+    const unsigned long long me = i < C ? sm.ck[i] : 0ull;
+    int r = 0;
+#pragma unroll 4
+    for (int j = 0; j < Cp; j += 2) {
+      const ulonglong2 x = *reinterpret_cast<const ulonglong2*>(&sm.ck[j]);
+      r += (x.x > me) + (x.y > me);
+    }
+    if (i < C && r < K) sm.ok[r] = me;
+  }
+  wave_lds_sync();
+  rk = lane < min(C, K) ? sm.ok[lane] : 0ull;
+  wave_lds_sync();  // sm is free again
+}
+
 // Top K of the candidates: element e of the lane when cand(e) (its key keyof(e), with
 // valid(e) marking the elements that exist at all), plus the carried key rk when
 // carry.  On return lane i < K holds the i-th largest key in rk; other lanes hold 0.
@@ -131,23 +161,7 @@ __device__ void rank_select(Valid valid, Cand cand, KeyOf keyof, bool carry,
       sm.ck[c ? o : kCap + lane] = keyof(e);
       o += c;
     }
-    const int Cp = (C + 1) & ~1;  // the counting loop reads two keys at a time
-    if (lane < Cp - C) sm.ck[C + lane] = 0ull;
-    wave_lds_sync();
-    for (int i0 = 0; i0 < C; i0 += kWave) {
-      const int i = i0 + lane;
-      const unsigned long long me = i < C ? sm.ck[i] : 0ull;
-      int r = 0;
-#pragma unroll 4
-      for (int j = 0; j < Cp; j += 2) {
-        const ulonglong2 x = *reinterpret_cast<const ulonglong2*>(&sm.ck[j]);
-        r += (x.x > me) + (x.y > me);
-      }
-      if (i < C && r < K) sm.ok[r] = me;
-    }
-    wave_lds_sync();
-    rk = lane < min(C, K) ? sm.ok[lane] : 0ull;
-    wave_lds_sync();  // sm is free again
+    rank_count(C, K, rk, sm);
   } else {
     unsigned long long taken = 0ull;  // bit e: element e taken
     bool carry_taken = false;         // the carried key taken
@@ -182,6 +196,81 @@ __device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long
   const unsigned long long t = th ? (unsigned long long)th << 32 : 1ull;
   rank_select<E>([&](int e) { return key[e] != 0ull; }, [&](int e) { return key[e] >= t; },
                  [&](int e) { return key[e]; }, rk >= t, rk, K, sm);
+}
+
+// Top K of one chunk of the logits row x, E per lane in v (element e of the lane has
+// id lo + ((e / 4) * 64 + lane) * 4 + e % 4; ids at or past vocab do not exist), with
+// m the lane's maximum (-inf over absent elements).  The result is wave_topk's on the
+// elements' keys, but the keys are formed for the candidates only: the bound th on
+// the upper key bits becomes a bound tau on the values (fkey is monotone; no NaNs),
+// each element slot is skipped by a uniform branch when no lane holds a candidate
+// there, and a lane's candidates are stored at offsets from a ballot's bit count.
+template <int E>
+__device__ void chunk_topk(const float (&v)[E], const float* __restrict__ x, int lo, int vocab, float m, int K,
+                           unsigned long long& rk, WaveLds& sm) {
+  const int lane = lane_id();
+  auto idof = [&](int e) { return lo + ((e / 4) * kWave + lane) * 4 + e % 4; };
+  const bool full = lo + kWave * E <= vocab;  // every element exists
+  // the lane maximum's upper key bits: 0 for a lane without elements (its first id is
+  // its smallest)
+  const unsigned mh = idof(0) < vocab ? fkey(m) : 0u;
+  const unsigned th = kth_upper(mh, K);
+  // keys >= th << 32 (>= 1 when th = 0) are the existing elements of value >= tau;
+  // at or below -inf's key (0x007fffff) every existing element qualifies
+  const float tau = th <= 0x007fffffu ? -INFINITY : unfkey(th);
+  auto cand = [&](int e) { return (full || idof(e) < vocab) && v[e] >= tau; };
+  int C = 0;  // candidates so far (uniform)
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool c = cand(e);
+    const unsigned long long msk = ballot(c);
+    if (msk) {
+      if (c) {
+        const int o = C + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(msk >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
+        if (o < kCap) sm.ck[o] = pack(v[e], idof(e));
+      }
+      C += (int)__popcll(msk);
+    }
+  }
+  rk = 0ull;
+  if (C <= kCap) {
+    rank_count(C, K, rk, sm);
+  } else {
+    // more than kCap candidates (many equal values): K rounds of a wave-wide maximum
+    // over the keys not taken yet.  The values are read again from the row, four at a
+    // time, in every round: keeping them or their keys live into this rare path took
+    // the kernel from 30 to over 100 registers (a third of its occupancy).
+    static_assert(E <= 32, "one bit per element");
+    unsigned taken = 0u;  // bit e: element e taken
+    unsigned long long out = 0ull;
+    for (int r = 0; r < K; ++r) {
+      unsigned long long b = 0ull;
+      int be = 0;
+#pragma unroll 1
+      for (int g = 0; g < E / 4; ++g) {  // four contiguous elements at a time
+        const int id0 = idof(4 * g);
+        float w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = id0 + q < vocab ? x[id0 + q] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = 4 * g + q;
+          const bool ok = id0 + q < vocab && !((taken >> e) & 1u);
+          const unsigned long long ke = ok ? pack(w[q], id0 + q) : 0ull;
+          if (ke > b) {
+            b = ke;
+            be = e;
+          }
+        }
+      }
+      const unsigned long long w = wave_max_u64(b);
+      if (w == 0ull) break;  // nothing left anywhere
+      if (b == w) taken |= 1u << be;  // keys are unique: one lane, one element
+      if (lane == r) out = w;
+    }
+    rk = out;
+  }
 }
 
 // One wave merges row `row`'s chunk lists (nchunks lists of k keys, each sorted best

@@ -75,6 +75,8 @@ const char* ddt_status_string(int status);
  *
  * logits     [rows, vocab] fp32, row r at logits + r * row_stride (row_stride >=
  *            vocab).  A row is one (sequence, position) pair: rows = S * L.
+ *            Finite values, or -inf for masked tokens; at least one finite value
+ *            per row, no NaN and no +inf (the softmax is undefined otherwise).
  * k          1 <= k <= min(vocab, DDT_MAX_K).
  * out_tok    [rows, k] int32: the k largest logits of the row, largest first;
  *            equal logits in increasing token id.
@@ -145,7 +147,8 @@ int ddt_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* nu
  * vocabulary chunks, then one workgroup per sequence that merges the chunks, builds
  * the tree and forms its mask).  Every output is bit-identical to the three calls.
  *
- * logits      [S, L, vocab] fp32; row (s, i) at logits + (s * L + i) * row_stride.
+ * logits      [S, L, vocab] fp32; row (s, i) at logits + (s * L + i) * row_stride;
+ *             values as for ddt_topk.
  * bonus       [S]; cu_prefix nullable [S+1] (needed for pos_ids).
  * Limits as for the three calls: 1 <= L <= DDT_MAX_L, 1 <= K <= min(vocab,
  * DDT_MAX_K), 0 <= B <= DDT_MAX_B.

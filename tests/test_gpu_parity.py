@@ -175,6 +175,40 @@ def test_edge_cases(name, kw, fused):
     run_case(cfg, fused=fused)
 
 
+def _tie_rows(kind, rows, V, rng):
+    if kind == "all-equal":
+        return np.full((rows, V), 0.5, dtype=np.float32)
+    if kind == "levels":        # a few distinct values: hundreds of ties in every chunk
+        return (np.round(rng.standard_normal((rows, V)) * 2.0) / 2.0).astype(np.float32)
+    if kind == "top-level":     # one value shared by a third of the row, the rest below it
+        x = rng.uniform(-8.0, -1.0, (rows, V)).astype(np.float32)
+        x[rng.random((rows, V)) < 1 / 3] = 2.0
+        return x
+    if kind == "neg-inf":       # mostly -inf, a few finite values, ties among them
+        x = np.full((rows, V), -np.inf, dtype=np.float32)
+        for r in range(rows):
+            idx = rng.choice(V, size=200, replace=False)
+            x[r, idx] = np.round(rng.standard_normal(200)).astype(np.float32)
+        return x
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["all-equal", "levels", "top-level", "neg-inf"])
+@pytest.mark.parametrize("rows,V,k", [(3, 4099, 8), (2, 3000, 64), (20, 70000, 32)])
+def test_topk_ties(kind, rows, V, k):
+    """Top-K of rows with heavy ties: chunks whose candidates exceed what the rank
+    count holds take the wave-maximum fallback.  Equal logits go to the smaller id;
+    tokens must match exactly.  V = 4099 leaves a ragged tail (scalar loads); 20 rows of
+    70000 use the 16-per-lane chunks."""
+    rng = np.random.default_rng(7 + rows + k)
+    x = _tie_rows(kind, rows, V, rng)
+    rt, rl = oracle.topk(x, k)
+    gt, gl = ddt.ddt_topk(dev_tensor(x), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(gt.cpu().numpy(), rt), kind
+    assert np.max(np.abs(gl.cpu().numpy().astype(np.float64) - rl)) <= TOPK_ATOL, kind
+
+
 def test_narrow_attention_groups():
     """A grid too large for one workgroup per CU: 4-wave row groups, two per CU, the last
     group of each (sequence, KV head) holding only the remainder rows (its other waves
