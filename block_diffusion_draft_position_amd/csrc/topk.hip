@@ -93,12 +93,15 @@ topk_merge(int nchunks, int k, const unsigned long long* __restrict__ cand,
 
 TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   TopkPlan p;
-  // chunk length: short chunks (more waves) for small problems, else 16 logits per
-  // lane.  32 per lane would halve the chunk lists to merge, but its 64-bit keys take
-  // 165 registers (two waves per SIMD instead of five), which measured slower: the
-  // draft side of C2 and C4 ran 5% and 11% faster with 16.
+  // chunk length: short chunks (more waves) for small problems, 32 logits per lane
+  // once that still gives four waves per CU (fewer, shorter chunk lists to merge: one
+  // merge batch for V = 128256; C2 +1.3% rounds/s over 16 per lane), else 16.  The
+  // chunk pass takes 46 registers at 32 per lane (eight waves per SIMD) because it
+  // forms keys for its candidates only.
   const int64_t full = 4 * (int64_t)cu_count();
-  p.e = rows * ceil_div(vocab, (int64_t)kWave * 8 * 2) < full ? 8 : 16;
+  p.e = rows * ceil_div(vocab, (int64_t)kWave * 8 * 2) < full ? 8
+        : rows * ceil_div(vocab, (int64_t)kWave * 32) < full  ? 16
+                                                              : 32;
   p.nchunks = (int)ceil_div(vocab, (int64_t)kWave * p.e);
   p.merge_e = k <= 8 ? 8 : k <= 32 ? 32 : 64;  // keys per lane: one chunk list each
   const size_t nslot = (size_t)rows * p.nchunks;
@@ -127,8 +130,10 @@ hipError_t launch_topk_partial(const float* logits, int64_t rows, int64_t vocab,
                      plan.nchunks, vec_ok, cand, stt)
   if (plan.e == 8)
     DDT_PART(8);
-  else
+  else if (plan.e == 16)
     DDT_PART(16);
+  else
+    DDT_PART(32);
 #undef DDT_PART
   return hipGetLastError();
 }

@@ -194,12 +194,12 @@ def _tie_rows(kind, rows, V, rng):
 
 
 @pytest.mark.parametrize("kind", ["all-equal", "levels", "top-level", "neg-inf"])
-@pytest.mark.parametrize("rows,V,k", [(3, 4099, 8), (2, 3000, 64), (20, 70000, 32)])
+@pytest.mark.parametrize("rows,V,k", [(3, 4099, 8), (2, 3000, 64), (20, 70000, 32), (20, 110000, 16)])
 def test_topk_ties(kind, rows, V, k):
     """Top-K of rows with heavy ties: chunks whose candidates exceed what the rank
     count holds take the wave-maximum fallback.  Equal logits go to the smaller id;
     tokens must match exactly.  V = 4099 leaves a ragged tail (scalar loads); 20 rows of
-    70000 use the 16-per-lane chunks."""
+    70000 use the 16-per-lane chunks, 20 rows of 110000 the 32-per-lane chunks."""
     rng = np.random.default_rng(7 + rows + k)
     x = _tie_rows(kind, rows, V, rng)
     rt, rl = oracle.topk(x, k)
