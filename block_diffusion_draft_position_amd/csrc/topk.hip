@@ -94,13 +94,14 @@ topk_merge(int nchunks, int k, const unsigned long long* __restrict__ cand,
 TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   TopkPlan p;
   // chunk length: short chunks (more waves) for small problems, 32 logits per lane
-  // once that still gives four waves per CU (fewer, shorter chunk lists to merge: one
-  // merge batch for V = 128256; C2 +1.3% rounds/s over 16 per lane), else 16.  The
-  // chunk pass takes 46 registers at 32 per lane (eight waves per SIMD) because it
-  // forms keys for its candidates only.
+  // once that still gives two waves per CU (fewer, shorter chunk lists to merge: one
+  // merge batch for V = 128256; over 16 per lane +1.3% rounds/s at C2, +0.9% and +1.5%
+  // at C3 with B = 512 and 64; C1 keeps 8, 2% ahead of 32), else 16.  The chunk pass
+  // takes 46 registers at 32 per lane (eight waves per SIMD) because it forms keys for
+  // its candidates only.
   const int64_t full = 4 * (int64_t)cu_count();
   p.e = rows * ceil_div(vocab, (int64_t)kWave * 8 * 2) < full ? 8
-        : rows * ceil_div(vocab, (int64_t)kWave * 32) < full  ? 16
+        : rows * ceil_div(vocab, (int64_t)kWave * 32) < full / 2 ? 16
                                                               : 32;
   p.nchunks = (int)ceil_div(vocab, (int64_t)kWave * p.e);
   p.merge_e = k <= 8 ? 8 : k <= 32 ? 32 : 64;  // keys per lane: one chunk list each
