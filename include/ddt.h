@@ -213,7 +213,7 @@ int ddt_tree_attention(const void* q, const void* k_cache, const void* v_cache,
  * tree_tok, parent  [S, N] from ddt_build_tree; num_nodes [S].
  * target_logits     [S, N, vocab] fp32 target logits at every node (rows past
  *                   num_nodes are not read).  Greedy = argmax, equal logits to the
- *                   smaller token id.
+ *                   smaller token id (-0 and +0 are equal).  No NaN.
  * accept_len [S]     accepted draft tokens a (the round emits a + 1 tokens).
  * acc_nodes  [S, L]  accepted node indices in order, -1 padded.
  * acc_tok    [S, L]  their tokens, -1 padded.
