@@ -206,8 +206,8 @@ __device__ void wave_topk(const unsigned long long (&key)[E], unsigned long long
 // each element slot is skipped by a uniform branch when no lane holds a candidate
 // there, and a lane's candidates are stored at offsets from a ballot's bit count.
 template <int E>
-__device__ void chunk_topk(const float (&v)[E], const float* __restrict__ x, int lo, int vocab, float m, int K,
-                           unsigned long long& rk, WaveLds& sm) {
+__device__ void chunk_topk(const float (&v)[E], const float* __restrict__ x, int lo, int vocab,
+                           float m, int K, unsigned long long& rk, WaveLds& sm) {
   const int lane = lane_id();
   auto idof = [&](int e) { return lo + ((e / 4) * kWave + lane) * 4 + e % 4; };
   const bool full = lo + kWave * E <= vocab;  // every element exists
@@ -226,8 +226,9 @@ __device__ void chunk_topk(const float (&v)[E], const float* __restrict__ x, int
     const unsigned long long msk = ballot(c);
     if (msk) {
       if (c) {
-        const int o = C + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(msk >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
+        // candidates in the lanes below this one
+        const unsigned below = __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u);
+        const int o = C + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(msk >> 32), below);
         if (o < kCap) sm.ck[o] = pack(v[e], idof(e));
       }
       C += (int)__popcll(msk);
