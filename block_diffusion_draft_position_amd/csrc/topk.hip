@@ -5,7 +5,8 @@
 // the K largest logits (larger first, equal logits by smaller id) and
 // log q = logit - logsumexp(row).
 //
-// Two kernels, one wave per workgroup, no atomics:
+// Two kernels, no atomics; every wave works on its own (four chunk waves share a
+// workgroup: C1 +1% rounds/s over one-wave workgroups):
 //   topk_partial  a wave owns a chunk of 64*E logits of one row and loads all of it
 //                 into registers with 16-byte loads issued together (one memory
 //                 latency per chunk).  It forms the chunk's max and sum of
@@ -28,14 +29,21 @@ namespace {
 
 using namespace topk;
 
+constexpr int kPartWaves = 4;  // chunk waves per workgroup, each on its own
+
 template <int E>
-__global__ void __launch_bounds__(kWave)
+__global__ void __launch_bounds__(kPartWaves * kWave)
 topk_partial(const float* __restrict__ logits, int64_t stride, int vocab, int k, int nchunks,
-             bool vec_ok, unsigned long long* __restrict__ cand, float2* __restrict__ stats) {
-  __shared__ WaveLds sm;
-  const int c = (int)(blockIdx.x % (unsigned)nchunks);
-  const int64_t row = blockIdx.x / (unsigned)nchunks;
-  const int lane = threadIdx.x;
+             int64_t nslots, bool vec_ok, unsigned long long* __restrict__ cand,
+             float2* __restrict__ stats) {
+  __shared__ WaveLds sms[kPartWaves];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t slot0 = (int64_t)blockIdx.x * kPartWaves + wave;  // (row, chunk) of this wave
+  if (slot0 >= nslots) return;
+  WaveLds& sm = sms[wave];
+  const int c = (int)(slot0 % nchunks);
+  const int64_t row = slot0 / nchunks;
+  const int lane = threadIdx.x % kWave;
   const float* x = logits + row * stride;
   const int lo = c * kWave * E;
 
@@ -125,10 +133,11 @@ hipError_t launch_topk_partial(const float* logits, int64_t rows, int64_t vocab,
   float2* stt;
   topk_ws_parts(ws, rows, k, plan, &cand, &stt);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && (stride % 4 == 0);
-  const dim3 grid((unsigned)(rows * plan.nchunks));
+  const int64_t nslots = rows * plan.nchunks;
+  const dim3 grid((unsigned)ceil_div(nslots, kPartWaves));
 #define DDT_PART(EE)                                                                            \
-  hipLaunchKernelGGL(topk_partial<EE>, grid, dim3(kWave), 0, st, logits, stride, (int)vocab, k, \
-                     plan.nchunks, vec_ok, cand, stt)
+  hipLaunchKernelGGL(topk_partial<EE>, grid, dim3(kPartWaves * kWave), 0, st, logits, stride,   \
+                     (int)vocab, k, plan.nchunks, nslots, vec_ok, cand, stt)
   if (plan.e == 8)
     DDT_PART(8);
   else if (plan.e == 16)
