@@ -25,7 +25,7 @@
 //   Online softmax runs in base 2 with scale * log2(e) folded into one multiply.
 //
 //   attn_d128 (D = 128): 32 query rows per wave as two blocks of 16, K/V tiles moved
-//   global -> LDS by DMA through a 4-stage ring, v_mfma_f32_16x16x32_bf16 for both
+//   global -> LDS by DMA through a 2-stage ring, v_mfma_f32_16x16x32_bf16 for both
 //   products, V^T read with the transposing LDS load (details at the kernel).
 //
 //   Partials are written with nontemporal stores: the combine reads each once, and
@@ -326,9 +326,11 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 // ---------------------------------------------------------------- bf16, D = 128 (gfx950 path)
 // Same decomposition as attn_partial_bf16, rebuilt around gfx950 features:
 //   * K and V tiles (64 keys) go global -> LDS with global_load_lds_dwordx4, no
-//     registers in between, into a 4-stage ring: three tiles are in flight while
-//     one is consumed, and one barrier per tile suffices (the stage being refilled
-//     was consumed one barrier earlier).  A 256-byte key row keeps its sixteen
+//     registers in between, into a 2-stage ring: tile t + 1 is issued right after
+//     the barrier that opens tile t, so one tile is in flight while one is consumed.
+//     One barrier per tile suffices: the stage refilled after barrier t was last
+//     read in tile t - 1, which every wave finished before arriving at barrier t.
+//     A 256-byte key row keeps its sixteen
 //     16-byte chunks XOR-swizzled (chunk c of key k at slot c ^ swz(k)) so that
 //     both the K reads and the transposed V reads are free of bank conflicts.
 //   * V stays row-major; the PV operand V^T is read with ds_read_b64_tr_b16, which

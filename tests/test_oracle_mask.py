@@ -31,9 +31,32 @@ def test_mask_closed_forms(L, K, B, seed):
         for j in range(n + 1, N):
             assert not (int(m[n, j // 32]) >> (j % 32)) & 1
     assert not np.any(m[nn:])
-    pos = oracle.position_ids(tree["depth"], nn, 100)
-    assert pos[:nn].tolist() == (100 + tree["depth"][:nn]).tolist()
+    # a node's position is where its token lands when its root-to-node path is laid
+    # out after the prefix as one plain sequence: the prefix holds P tokens and the
+    # path holds popcount(mask row) tokens (the root b included), so the node's token
+    # is the last of P + popcount entries (運作流程 step 3 scores each node as the
+    # continuation of the context by its path)
+    P = 100
+    pos = oracle.position_ids(tree["depth"], nn, P)
+    for n in range(nn):
+        assert pos[n] == P + _popcount(m[n]) - 1
+        assert pos[n] == P + len(oracle.ancestors(tree["parent"], n)) - 1
     assert np.all(pos[nn:] == -1)
+
+
+@pytest.mark.parametrize("P", [0, 1, 37, 4096])
+def test_positions_of_a_chain_are_plain_decoding(P):
+    """K = 1 makes the tree a single path (the single-path verification the DDTree
+    page's 核心創新 contrasts with): the positions must then be those plain
+    one-token-at-a-time decoding gives b, c_1, c_2, ...: P, P + 1, P + 2, ..."""
+    L = 9
+    cfg = configs.custom("chain", L=L, V=50, K=1, B=L)
+    d = gen.draft(cfg, 4, 0)
+    tok, lq = oracle.topk(d["logits"], 1)
+    tree = oracle.build_tree(tok, lq, d["bonus"], L)
+    assert int(tree["num_nodes"]) == L + 1
+    pos = oracle.position_ids(tree["depth"], L + 1, P)
+    assert pos.tolist() == list(range(P, P + L + 1))
 
 
 def test_word_boundaries():
