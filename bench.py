@@ -1,15 +1,18 @@
 """Benchmark: DDTree verification rounds per second on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload C1]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload C4]
 
 A step is one whole verification round for every sequence of the workload:
 ddt_topk -> ddt_build_tree -> ddt_tree_mask -> ddt_tree_attention -> ddt_tree_walk,
 on inputs already resident in HBM, replayed from HIP graphs.  Enough copies of the
-inputs are rotated that the working set exceeds the 256 MB Infinity Cache.
+inputs are rotated that the working set exceeds the 256 MB Infinity Cache.  The
+default workload is the largest one: 32 sequences with 16K-32K prefixes, V = 128256,
+Hq = 64, Hkv = 8, D = 128, bf16.
 
-Prints one JSON line: rounds/s, the attention kernel's live roofline (HIP events
-around that kernel inside the timed region), and the CPU oracle's rate on a bounded
-sample of the same workload, timed on this host.
+Prints one JSON line: rounds/s, the attention main kernel's roofline (HIP events
+attached to its dispatches), the whole attention step (main kernel and split merge)
+next to it, and the CPU oracle's rate on a bounded sample of the same workload,
+timed on this host's cores.
 """
 import argparse
 import json
@@ -57,19 +60,38 @@ def describe(cfg):
 
 
 def attention_cost(cfg, prefix_lens):
-    """Algorithmic HBM bytes and flops of one attention main-kernel launch: it reads
-    every prefix K/V row once per KV head, the tree K/V, Q and the mask.  Flops are
-    QK^T and PV over prefix plus ancestors (ancestors counted as depth+1 <= L+1 keys
-    at most; the prefix dominates)."""
+    """Algorithmic HBM bytes and flops of one tree-attention call: every prefix K/V
+    row read once per KV head, the tree K/V, Q and the mask read once, the output O
+    written once.  Flops are QK^T and PV over the prefix (the ancestors add at most
+    L + 1 keys per row; the prefix dominates)."""
     e = 2 if cfg.dtype == "bf16" else 4
     N, W = cfg.N, cfg.W
     P = int(np.sum(prefix_lens))
     kv = P * cfg.Hkv * cfg.D * e * 2
     tree = cfg.S * N * cfg.Hkv * cfg.D * e * 2
     q = cfg.S * N * cfg.Hq * cfg.D * e
+    o = cfg.S * N * cfg.Hq * cfg.D * e
     mask = cfg.S * N * W * 4
     flops = 4.0 * N * cfg.Hq * cfg.D * P
-    return kv + tree + q + mask, flops
+    return kv + tree + q + o + mask, flops
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def attention_kernel(cfg):
@@ -104,15 +126,17 @@ def measured_traffic(workload):
 
 
 def cpu_baseline(cfg, b, att, budget_s=12.0):
-    """The oracle as it stands, single-threaded, on a bounded sample of the workload,
-    scaled to rounds/s: steps 1-3 and the walk for one sequence, attention for a
-    sample of that sequence's rows; the rest is extrapolated linearly."""
+    """The oracle as it stands on a bounded sample of the workload, scaled to
+    rounds/s: steps 1-3 and the walk for one sequence, attention for a sample of that
+    sequence's rows; the rest is extrapolated linearly.  Its numpy BLAS calls may use
+    every core this process may run on; its Python loops run on one."""
     from threadpoolctl import threadpool_limits
 
     import oracle
     scale = 1.0 / math.sqrt(cfg.D)
     s = 0
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         tok, lq = oracle.topk(b["draft_logits"][s], cfg.K)
         tree = oracle.build_tree(tok, lq, int(b["bonus"][s]), cfg.B)
@@ -139,11 +163,12 @@ def cpu_baseline(cfg, b, att, budget_s=12.0):
             done += len(chunk)
     total_rows = cfg.S * cfg.N * cfg.Hq
     per_round = cfg.S * t_steps + t_att / done * total_rows
-    return {"value": 1.0 / per_round, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+    return {"value": 1.0 / per_round, "unit": "rounds/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": (f"sequence 0 of {cfg.S}: top-K, tree, mask and walk in full, tree attention "
                        f"for {done} of its {nn * cfg.Hq} (node, head) rows; scaled linearly to "
-                       f"{cfg.S} sequences x {total_rows // cfg.S} rows; fp64 numpy, 1 thread, "
-                       f"{cfg.S * t_steps + t_att / done * total_rows:.3g} s per round")}
+                       f"{cfg.S} sequences x {total_rows // cfg.S} rows; fp64 numpy with BLAS on "
+                       f"{cores} threads (Python loops on one), {per_round:.3g} s per round")}
 
 
 def main():
@@ -151,7 +176,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C1", help="one of " + ", ".join(sorted(configs.CONFIGS)))
+    ap.add_argument("--workload", default="C4", help="one of " + ", ".join(sorted(configs.CONFIGS)))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
@@ -172,7 +197,8 @@ def main():
     att = attempts_for(cfg)
     log(f"[bench] generating {describe(cfg)}")
     t0 = time.time()
-    b = gen.batch(cfg, att)
+    workers = min(16, host_cores())
+    b = gen.batch(cfg, att, workers=workers)
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
 
     def up(x):
@@ -192,8 +218,13 @@ def main():
     torch.cuda.synchronize()
     tt, par, nn = (rnd.tree[k].cpu().numpy() for k in ("tree_tok", "parent", "num_nodes"))
     tl = np.zeros((cfg.S, cfg.N, cfg.V), dtype=np.float32)
-    for s in range(cfg.S):
+
+    def target_of(s):
         gen.target_logits(cfg, s, att[s], tt[s], par[s], int(nn[s]), b["chain"][s], b["keep"][s], out=tl[s])
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(target_of, range(cfg.S)))
     base["target"] = up(tl)
     del tl
     per_copy = sum(t.numel() * t.element_size() for t in base.values())
@@ -237,7 +268,7 @@ def main():
     for i in range(nprof):
         step(copies[i % ncopies])
     torch.cuda.synchronize()
-    attn_ms, attn_n = ddt.attention_timing()
+    attn_ms, step_ms, attn_n = ddt.attention_timing()
     ddt.attention_profiling(False)
     del graphs
     acc = rnd.walk["accept_len"].float().mean().item()
@@ -254,6 +285,8 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / attn_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(cfg.name)
+    step_s = step_ms / max(attn_n, 1) / 1e3
+    step_ach = (bytes_ / step_s / 1e9) if roof["bound"] == "hbm" else (flops / step_s / 1e12)
     roof["kernel"] = attention_kernel(cfg)
     roof["kernel_us"] = attn_s * 1e6
     roof["launches_timed"] = attn_n
@@ -271,6 +304,11 @@ def main():
                    "kv_heads": cfg.Hkv, "head_dim": cfg.D, "rows_per_kv_head": R,
                    "input_copies": ncopies, "graph_replay": not args.no_graph},
         "roofline": roof,
+        "attention_step": {"kernels": [roof["kernel"], "attn_combine"] if cfg.dtype == "bf16" else [roof["kernel"]],
+                           "us": step_s * 1e6, "achieved": step_ach, "unit": roof["unit"],
+                           "frac": step_ach / roof["peak"],
+                           "timing": "main kernel start to split-merge end, HIP events attached to "
+                                     "the two dispatches, same eager rounds"},
         "accept_len_mean": acc,
     }
     if not args.no_cpu_baseline:

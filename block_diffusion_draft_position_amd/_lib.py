@@ -52,7 +52,8 @@ def load() -> ctypes.CDLL:
         "ddt_tree_walk_workspace_size": (sz, [i32, i32, i64]),
         "ddt_tree_walk": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]),
         "ddt_attention_profiling": (i32, [i32]),
-        "ddt_attention_timing": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
+        "ddt_attention_timing": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -269,8 +270,10 @@ def attention_profiling(enable: bool):
     _check(load().ddt_attention_profiling(1 if enable else 0), "ddt_attention_profiling")
 
 
-def attention_timing() -> Tuple[float, int]:
-    """(summed milliseconds, launches) of the attention main kernel since the last read."""
-    t, n = ctypes.c_double(0.0), ctypes.c_int(0)
-    _check(load().ddt_attention_timing(ctypes.byref(t), ctypes.byref(n)), "ddt_attention_timing")
-    return t.value, n.value
+def attention_timing() -> Tuple[float, float, int]:
+    """(summed milliseconds of the main kernel, summed milliseconds of the whole
+    attention step, calls) since the last read."""
+    tm, ts, n = ctypes.c_double(0.0), ctypes.c_double(0.0), ctypes.c_int(0)
+    _check(load().ddt_attention_timing(ctypes.byref(tm), ctypes.byref(ts), ctypes.byref(n)),
+           "ddt_attention_timing")
+    return tm.value, ts.value, n.value

@@ -13,7 +13,6 @@ namespace tree {
 
 constexpr int kRankCap = 256;  // final rounds with at most this many candidates rank them exactly
 constexpr int kGatherCap = 2048;  // radix selects over at most this many keys read them from LDS
-constexpr unsigned long long kIdxMask = 0x3ffull;  // low key bits that carry the node-order number
 
 struct TreeSmem {
   unsigned long long* key;  // [kGatherCap] final-round candidate keys
@@ -265,13 +264,9 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
           }
         }
       }
-      // Candidate keys: the score's order-preserving 64 bits with the lowest ten replaced
-      // by the complement of the candidate's node-order number, so keys are unique and
-      // scores that tie (to 2^-42 relative) go in node order.
-      // candidate i of stream j (rank cur + i) scoring v
-      auto ukey = [&](int j, int i, double v) -> unsigned long long {
-        return (key_of(v) & ~kIdxMask) | (kIdxMask - (unsigned long long)(off[j] + i));
-      };
+      // Candidate keys: the fp64 score's order-preserving 64 bits.  Candidate i of
+      // stream j (rank cur + i) has node-order number off[j] + i (parent's selection
+      // order, then rank); equal scores are taken in that order, in every cut below.
       if (total <= kRankCap) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -279,39 +274,56 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
 #pragma unroll
             for (int r = 0; r < KW; ++r)
               if (r >= cur[j] && r < cur[j] + cnt[j])
-                sm.key[off[j] + r - cur[j]] = ukey(j, r - cur[j], sc[j] + (double)rowv[j][r]);
+                sm.key[off[j] + r - cur[j]] = key_of(sc[j] + (double)rowv[j][r]);
           } else {
             for (int i = 0; i < cnt[j]; ++i)
-              sm.key[off[j] + i] = ukey(j, i, sc[j] + lq(dep[j], cur[j] + i));
+              sm.key[off[j] + i] = key_of(sc[j] + lq(dep[j], cur[j] + i));
           }
         }
         if (total <= kWave) {
-          // one candidate per lane: the R-th largest key by a ballot search two bits at
-          // a time (three independent ballots per step), stopping once exactly R keys
-          // reach the prefix; each stream then keeps its candidates at or above it
+          // one candidate per lane (lane = node-order number): the R-th largest key t by
+          // a ballot search two bits at a time (three independent ballots per step),
+          // stopping once exactly R keys reach the prefix.  If more than R keys are >= t,
+          // the keys equal to t tie at the boundary and the lowest lanes among them fill
+          // the budget.  Each stream then keeps its candidates in the taken set.
           sync();
           const bool has = lane < total;
           const unsigned long long mk = has ? sm.key[lane] : 0ull;
           unsigned long long t = 0ull;
+          int nge = total;  // keys >= t
           for (int b = 62; b >= 0; b -= 2) {
             const unsigned long long c1 = t | (1ull << b), c2 = t | (2ull << b), c3 = t | (3ull << b);
             // mk = 0 where no candidate, below every threshold
             const int n1 = __popcll(ballot(mk >= c1));
             const int n2 = __popcll(ballot(mk >= c2));
             const int n3 = __popcll(ballot(mk >= c3));
-            int nb = R + 1;
             if (n3 >= R) {
               t = c3;
-              nb = n3;
+              nge = n3;
             } else if (n2 >= R) {
               t = c2;
-              nb = n2;
+              nge = n2;
             } else if (n1 >= R) {
               t = c1;
-              nb = n1;
+              nge = n1;
             }
-            if (nb == R) break;
+            if (nge == R) break;
           }
+          // lanes holding t that are taken: all of them, or the lowest R - (keys > t)
+          unsigned long long eqt = ballot(has && mk == t);
+          if (nge > R) {
+            int need = R - __popcll(ballot(mk > t));
+            unsigned long long keep = 0ull;
+            for (; need > 0; --need) {
+              const unsigned long long low = eqt & (~eqt + 1ull);
+              keep |= low;
+              eqt ^= low;
+            }
+            eqt = keep;
+          }
+          auto taken = [&](unsigned long long key, int idx) {
+            return key > t || (key == t && ((eqt >> idx) & 1ull));
+          };
 #pragma unroll
           for (int j = 0; j < J; ++j) {
             int c = 0;
@@ -319,15 +331,17 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
 #pragma unroll
               for (int r = 0; r < KW; ++r)
                 c += r >= cur[j] && r < cur[j] + cnt[j] &&
-                     ukey(j, r - cur[j], sc[j] + (double)rowv[j][r]) >= t;
+                     taken(key_of(sc[j] + (double)rowv[j][r]), off[j] + r - cur[j]);
             } else {
-              for (int i = 0; i < cnt[j]; ++i) c += ukey(j, i, sc[j] + lq(dep[j], cur[j] + i)) >= t;
+              for (int i = 0; i < cnt[j]; ++i)
+                c += taken(key_of(sc[j] + lq(dep[j], cur[j] + i)), off[j] + i);
             }
             cnt[j] = c;
           }
           sync();  // sm.key is read again by the next cut
         } else {
-          // exact ranks: each candidate counts the keys above its own
+          // exact ranks: each candidate counts the keys above its own and the equal keys
+          // of lower node order
           const int Tp = (total + 7) & ~7;
           if (lane < Tp - total) sm.key[total + lane] = 0ull;  // below every real key
           sync();
@@ -340,7 +354,7 @@ __device__ __forceinline__ int build(TreeSmem& sm, int L, int K, int B, int bonu
 #pragma unroll
               for (int u = 0; u < 8; ++u) kj[u] = sm.key[j0 + u];
 #pragma unroll
-              for (int u = 0; u < 8; ++u) r += kj[u] > mk;
+              for (int u = 0; u < 8; ++u) r += kj[u] > mk || (kj[u] == mk && j0 + u < i);
             }
             if (i < total) sm.sel[i] = r < R;
           }

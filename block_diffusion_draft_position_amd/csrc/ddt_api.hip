@@ -30,10 +30,14 @@ int cu_count() {
 }
 
 namespace {
+struct ProfEvents {
+  hipEvent_t start, stop, step_stop;
+  bool step_used;
+};
 struct Prof {
   std::mutex mu;
   bool on = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  std::vector<ProfEvents> pool;
   size_t used = 0;
 };
 Prof& prof() {
@@ -42,22 +46,25 @@ Prof& prof() {
 }
 }  // namespace
 
-bool prof_events(hipEvent_t* start, hipEvent_t* stop) {
+bool prof_events(hipEvent_t* start, hipEvent_t* stop, hipEvent_t* step_stop) {
   Prof& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
   if (!p.on) return false;
   if (p.used == p.pool.size()) {
-    hipEvent_t a = nullptr, b = nullptr;
-    if (hipEventCreate(&a) != hipSuccess) return false;
-    if (hipEventCreate(&b) != hipSuccess) {
-      (void)hipEventDestroy(a);
-      return false;
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    for (int i = 0; i < 3; ++i) {
+      if (hipEventCreate(&ev[i]) != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+        return false;
+      }
     }
-    p.pool.emplace_back(a, b);
+    p.pool.push_back({ev[0], ev[1], ev[2], false});
   }
-  auto& ev = p.pool[p.used++];
-  *start = ev.first;
-  *stop = ev.second;
+  auto& e = p.pool[p.used++];
+  e.step_used = step_stop != nullptr;
+  *start = e.start;
+  *stop = e.stop;
+  if (step_stop) *step_stop = e.step_stop;
   return true;
 }
 
@@ -221,10 +228,9 @@ int ddt_attention_profiling(int enable) {
   p.on = enable != 0;
   if (!p.on) {
     int rc = DDT_OK;
-    for (auto& ev : p.pool) {
-      if (hipEventDestroy(ev.first) != hipSuccess) rc = DDT_ERR_HIP;
-      if (hipEventDestroy(ev.second) != hipSuccess) rc = DDT_ERR_HIP;
-    }
+    for (auto& ev : p.pool)
+      for (hipEvent_t e : {ev.start, ev.stop, ev.step_stop})
+        if (hipEventDestroy(e) != hipSuccess) rc = DDT_ERR_HIP;
     p.pool.clear();
     p.used = 0;
     return rc;
@@ -232,21 +238,26 @@ int ddt_attention_profiling(int enable) {
   return DDT_OK;
 }
 
-int ddt_attention_timing(double* total_ms, int* count) {
-  if (!total_ms || !count) return DDT_ERR_INVALID_ARG;
+int ddt_attention_timing(double* main_ms, double* step_ms, int* count) {
+  if (!main_ms || !step_ms || !count) return DDT_ERR_INVALID_ARG;
   Prof& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
-  double t = 0.0;
+  double tm = 0.0, ts = 0.0;
   int n = 0;
   for (size_t i = 0; i < p.used; ++i) {
-    if (hipEventSynchronize(p.pool[i].second) != hipSuccess) return DDT_ERR_HIP;
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, p.pool[i].first, p.pool[i].second) != hipSuccess) return DDT_ERR_HIP;
-    t += ms;
+    const ProfEvents& e = p.pool[i];
+    const hipEvent_t last = e.step_used ? e.step_stop : e.stop;
+    if (hipEventSynchronize(last) != hipSuccess) return DDT_ERR_HIP;
+    float a = 0.f, b = 0.f;
+    if (hipEventElapsedTime(&a, e.start, e.stop) != hipSuccess) return DDT_ERR_HIP;
+    if (hipEventElapsedTime(&b, e.start, last) != hipSuccess) return DDT_ERR_HIP;
+    tm += a;
+    ts += b;
     ++n;
   }
   p.used = 0;
-  *total_ms = t;
+  *main_ms = tm;
+  *step_ms = ts;
   *count = n;
   return DDT_OK;
 }

@@ -210,11 +210,14 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             int32_t* acc_tok, int32_t* bonus_out, void* ws, const WalkPlan& plan,
                             hipStream_t st);
 
-// Benchmark timing of the attention's main kernel (see ddt_attention_profiling).
-// While profiling is on, prof_events hands out a start/stop event pair that the
-// launch attaches to the kernel's dispatch (hipExtLaunchKernelGGL), so the pair
-// brackets the kernel's execution, not its enqueueing; otherwise it returns false.
-bool prof_events(hipEvent_t* start, hipEvent_t* stop);
+// Benchmark timing of the attention's main kernel and of the whole attention step
+// (see ddt_attention_profiling).  While profiling is on, prof_events hands out a
+// start/stop event pair that the launch attaches to the main kernel's dispatch
+// (hipExtLaunchKernelGGL), so the pair brackets the kernel's execution, not its
+// enqueueing; a launch that runs a second kernel (the split merge) asks for
+// step_stop too and attaches it as that kernel's stop event.  Without profiling it
+// returns false.
+bool prof_events(hipEvent_t* start, hipEvent_t* stop, hipEvent_t* step_stop);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -978,7 +978,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   if (p.dtype == DDT_F32) {
     const int64_t rows = (int64_t)S * N * Hq;
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    if (!prof_events(&ev0, &ev1)) ev0 = ev1 = nullptr;
+    if (!prof_events(&ev0, &ev1, nullptr)) ev0 = ev1 = nullptr;
 #define DDT_F32_D(DD)                                                                          \
   case DD:                                                                                     \
     hipExtLaunchKernelGGL(attn_f32<DD>, dim3((unsigned)rows), dim3(64), 0, st, ev0, ev1, 0,    \
@@ -997,8 +997,8 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   float* opart = static_cast<float*>(ws);
   float2* ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align_up(rows * D * sizeof(float), 256));
   hipError_t e;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (!prof_events(&ev0, &ev1)) ev0 = ev1 = nullptr;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr, ev2 = nullptr;
+  if (!prof_events(&ev0, &ev1, &ev2)) ev0 = ev1 = ev2 = nullptr;
   switch (D) {
     case 32: e = launch_partial_d<32>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
     case 64: e = launch_partial_d<64>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
@@ -1012,10 +1012,10 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   // splits per batch: enough for every split of a row when that fits in registers
   const int nused = p.nsplit + 1;
   const int kb = nused <= 2 ? 2 : nused <= 4 ? 4 : nused <= 8 ? 8 : nused <= 16 ? 16 : 32;
-#define DDT_COMB_KB(DD, KK)                                                                          \
-  hipLaunchKernelGGL((attn_combine<bf16_t, DD, KK>), dim3(blocks), dim3(kCombineThreads), 0, st, opart, ml,      \
-                     cu_prefix, num_nodes, S, N, Hq, Hkv, p.G, p.rows_pad, p.nsplit, p.chunk,        \
-                     kc != nullptr, (bf16_t*)out, lse)
+#define DDT_COMB_KB(DD, KK)                                                                     \
+  hipExtLaunchKernelGGL((attn_combine<bf16_t, DD, KK>), dim3(blocks), dim3(kCombineThreads), 0, \
+                        st, nullptr, ev2, 0, opart, ml, cu_prefix, num_nodes, S, N, Hq, Hkv,    \
+                        p.G, p.rows_pad, p.nsplit, p.chunk, kc != nullptr, (bf16_t*)out, lse)
 #define DDT_COMB(DD)                                     \
   case DD:                                               \
     switch (kb) {                                        \

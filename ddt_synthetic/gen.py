@@ -146,12 +146,14 @@ def target_logits(cfg: Config, seq: int, attempt: int, tree_tok: np.ndarray, par
 
 # ----------------------------------------------------------------------------- batches
 def batch(cfg: Config, attempts: Optional[Sequence[int]] = None,
-          with_qkv: bool = True) -> Dict[str, np.ndarray]:
+          with_qkv: bool = True, workers: int = 1) -> Dict[str, np.ndarray]:
     """All S sequences of one workload, stacked in the layouts the library takes.
 
     draft_logits [S,L,V] f32; bonus [S] i32; chain [S,L+1]; keep [S,L+1];
     prefix_lens [S]; cu_prefix [S+1] i64; q [S,N,Hq,D]; k_cache/v_cache
     [sum P, Hkv, D] (sequences packed back to back); k_tree/v_tree [S,N,Hkv,D].
+    ``workers`` > 1 draws the sequences' attention operands on that many threads
+    (each sequence has its own seed, so the arrays are the same either way).
     """
     S = cfg.S
     if attempts is None:
@@ -179,12 +181,20 @@ def batch(cfg: Config, attempts: Optional[Sequence[int]] = None,
         vc = np.empty_like(kc)
         kt = np.empty((S, cfg.N, cfg.Hkv, cfg.D), dtype=et)
         vt = np.empty_like(kt)
-        for s in range(S):
+        def fill(s):
             x = qkv(cfg, s, int(P[s]))
             q[s] = x["q"]
             kc[cu[s]:cu[s + 1]] = x["k_prefix"]
             vc[cu[s]:cu[s + 1]] = x["v_prefix"]
             kt[s] = x["k_tree"]
             vt[s] = x["v_tree"]
+
+        if workers > 1 and S > 1:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(max_workers=min(workers, S)) as ex:
+                list(ex.map(fill, range(S)))
+        else:
+            for s in range(S):
+                fill(s)
         out.update(q=q, k_cache=kc, v_cache=vc, k_tree=kt, v_tree=vt)
     return out

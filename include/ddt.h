@@ -232,19 +232,21 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                   void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- benchmark aid
- * Timing of the attention's main kernel (the round's dominant kernel) with HIP
- * events on the stream it runs on.  While profiling is on, every
- * ddt_tree_attention call attaches a start/stop event pair to that kernel's
- * dispatch (hipExtLaunchKernelGGL), so the pair brackets the kernel's execution.
- * Use it on eagerly launched calls: event pairs recorded during a HIP graph
- * capture are not readable afterwards.  ddt_attention_timing waits for the
- * recorded pairs, returns the sum of their elapsed times in milliseconds and their
- * count, and forgets them.  ddt_attention_profiling(0) releases the events.  This
- * is the only state the library keeps; it is process-wide and guarded by a mutex.
- * Returns DDT_OK or DDT_ERR_HIP.
+ * Timing of the attention step (the round's dominant cost) with HIP events on the
+ * stream it runs on.  While profiling is on, every ddt_tree_attention call attaches
+ * a start/stop event pair to its main kernel's dispatch (hipExtLaunchKernelGGL), so
+ * the pair brackets that kernel's execution, and a third event to the stop of the
+ * split-merge kernel that completes the step (for fp32 inputs the step is the one
+ * kernel).  Use it on eagerly launched calls: events recorded during a HIP graph
+ * capture are not readable afterwards.  ddt_attention_timing waits for the recorded
+ * calls and returns, summed over them in milliseconds, the main kernel's time and
+ * the whole step's (main kernel start to merge end), with their count, and forgets
+ * them.  ddt_attention_profiling(0) releases the events.  This is the only state
+ * the library keeps; it is process-wide and guarded by a mutex.
+ * Returns DDT_OK, DDT_ERR_INVALID_ARG (null pointer) or DDT_ERR_HIP.
  */
 int ddt_attention_profiling(int enable);
-int ddt_attention_timing(double* total_ms, int* count);
+int ddt_attention_timing(double* main_ms, double* step_ms, int* count);
 
 #ifdef __cplusplus
 }

@@ -331,7 +331,8 @@ def test_deterministic():
 
 # ----------------------------------------------------------------------------- full workloads
 @pytest.mark.parametrize("name,rows", [("C0", None), ("C1", 200), ("C2", 48), ("C3-B16", 64),
-                                       ("C3-B128", 64), ("C3-B512", 64), ("C4", 12)])
+                                       ("C3-B32", 64), ("C3-B64", 64), ("C3-B128", 64),
+                                       ("C3-B256", 64), ("C3-B512", 64), ("C4", 12)])
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
 def test_full_workloads(name, rows, fused):
     run_case(configs.get(name), rows_per_seq=rows, fused=fused)
