@@ -51,6 +51,8 @@ def load() -> ctypes.CDLL:
                                      f32, i64, vp, vp, vp, sz, vp]),
         "ddt_tree_walk_workspace_size": (sz, [i32, i32, i64]),
         "ddt_tree_walk": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]),
+        "ddt_tree_walk_noalloc_max_bytes": (sz, []),
+        "ddt_tree_walk_noalloc": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp]),
         "ddt_attention_profiling": (i32, [i32]),
         "ddt_attention_timing": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int)]),
@@ -66,8 +68,8 @@ def load() -> ctypes.CDLL:
 EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_build_tree",
            "ddt_tree_mask", "ddt_draft_tree_workspace_size", "ddt_draft_tree",
            "ddt_tree_attention_workspace_size", "ddt_tree_attention",
-           "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_attention_profiling",
-           "ddt_attention_timing")
+           "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_tree_walk_noalloc_max_bytes",
+           "ddt_tree_walk_noalloc", "ddt_attention_profiling", "ddt_attention_timing")
 
 
 def _check(status: int, what: str):
@@ -263,6 +265,30 @@ def ddt_tree_walk(tree_tok, parent, num_nodes, target_logits, L: int, out=None, 
     _check(lib.ddt_tree_walk(_p(tree_tok), _p(parent), _p(num_nodes), _p(target_logits), S, N - 1,
                              L, V, _p(out["accept_len"]), _p(out["acc_nodes"]), _p(out["acc_tok"]),
                              _p(out["bonus"]), _p(ws), ws.numel(), _stream(dev)), "ddt_tree_walk")
+    return out
+
+
+def ddt_tree_walk_noalloc(tree_tok, parent, num_nodes, target_logits, L: int, out=None):
+    """ddt_tree_walk on the library's static workspace (no allocation in the call)."""
+    lib = load()
+    S, N = tree_tok.shape
+    _dev(tree_tok, "tree_tok", torch.int32)
+    _dev(parent, "parent", torch.int32, (S, N))
+    _dev(num_nodes, "num_nodes", torch.int32, (S,))
+    _dev(target_logits, "target_logits", torch.float32)
+    if target_logits.shape[:2] != (S, N):
+        raise ValueError("target_logits must be [S, N, V]")
+    V = target_logits.shape[2]
+    dev = tree_tok.device
+    if out is None:
+        out = {"accept_len": torch.empty(S, dtype=torch.int32, device=dev),
+               "acc_nodes": torch.empty(S, L, dtype=torch.int32, device=dev),
+               "acc_tok": torch.empty(S, L, dtype=torch.int32, device=dev),
+               "bonus": torch.empty(S, dtype=torch.int32, device=dev)}
+    _check(lib.ddt_tree_walk_noalloc(_p(tree_tok), _p(parent), _p(num_nodes), _p(target_logits), S,
+                                     N - 1, L, V, _p(out["accept_len"]), _p(out["acc_nodes"]),
+                                     _p(out["acc_tok"]), _p(out["bonus"]), _stream(dev)),
+           "ddt_tree_walk_noalloc")
     return out
 
 

@@ -88,6 +88,7 @@ const char* ddt_status_string(int status) {
     case DDT_ERR_UNSUPPORTED: return "unsupported configuration";
     case DDT_ERR_WORKSPACE: return "workspace too small";
     case DDT_ERR_HIP: return "HIP launch failure";
+    case DDT_ERR_TOO_LARGE: return "problem larger than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -220,6 +221,26 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                                      accept_len, acc_nodes, acc_tok, bonus_out, ws, plan,
                                      as_stream(stream)));
 }
+
+int ddt_tree_walk_noalloc(const int32_t* tree_tok, const int32_t* parent, const int32_t* num_nodes,
+                          const float* target_logits, int S, int B, int L, int64_t vocab,
+                          int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok,
+                          int32_t* bonus_out, void* stream) {
+  if (!tree_tok || !parent || !num_nodes || !target_logits || !accept_len || !acc_nodes ||
+      !acc_tok || !bonus_out)
+    return DDT_ERR_INVALID_ARG;
+  if (S < 1 || L < 1 || L > DDT_MAX_L || B < 0 || B > DDT_MAX_B || vocab < 1 || vocab > INT32_MAX)
+    return DDT_ERR_INVALID_ARG;
+  const WalkPlan plan = walk_plan(S, B, vocab);
+  if (plan.ws_bytes > walk_scratch_bytes()) return DDT_ERR_TOO_LARGE;
+  const hipStream_t st = as_stream(stream);
+  void* ws = nullptr;
+  if (walk_scratch(&ws, st) != hipSuccess) return DDT_ERR_HIP;
+  return hip_status(launch_tree_walk(tree_tok, parent, num_nodes, target_logits, S, B, L, vocab,
+                                     accept_len, acc_nodes, acc_tok, bonus_out, ws, plan, st));
+}
+
+size_t ddt_tree_walk_noalloc_max_bytes(void) { return walk_scratch_bytes(); }
 
 // ------------------------------------------------------------------ benchmark aid
 int ddt_attention_profiling(int enable) {

@@ -204,6 +204,11 @@ struct WalkPlan {
   size_t ws_bytes;       // counters + row counters + one 64-bit arg-max key per node
 };
 WalkPlan walk_plan(int S, int B, int64_t vocab);
+// The walk's static scratch (a file-scope device array of walk_scratch_bytes()): its
+// device address on the current device, looked up with hipGetSymbolAddress once per
+// device, whose first lookup also enqueues a zero fill on st.
+size_t walk_scratch_bytes();
+hipError_t walk_scratch(void** ptr, hipStream_t st);
 hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             const int32_t* num_nodes, const float* target, int S, int B, int L,
                             int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,

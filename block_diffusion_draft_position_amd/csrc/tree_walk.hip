@@ -24,10 +24,17 @@
 // 2080 rounds/s against 5950 (C1 -8%), so the ordering rests on the hardware's.
 #include <limits.h>
 
+#include <mutex>
+
 #include "ddt_internal.h"
 
 namespace ddt {
 namespace {
+
+// Workspace of the allocation-free walk entry point: one copy per GPU, zero at module
+// load, and every walk leaves what it used zero again.
+constexpr size_t kWalkScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kWalkScratchBytes];
 
 constexpr int kMaxWaves = 16;  // waves per workgroup
 constexpr int kE = 32;         // logits per lane per batch
@@ -215,7 +222,40 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   }
 }
 
+__global__ void __launch_bounds__(256) zero_fill(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
 }  // namespace
+
+size_t walk_scratch_bytes() { return kWalkScratchBytes; }
+
+hipError_t walk_scratch(void** ptr, hipStream_t st) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    // the array's device address on this device; the host-side name is not one
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // cleared once on this device, on the caller's stream, before its first walk (a
+    // fill kernel, not a memset, so that a call under stream capture records it too)
+    hipLaunchKernelGGL(zero_fill, dim3(256), dim3(256), 0, st, static_cast<uint4*>(p),
+                       kWalkScratchBytes / sizeof(uint4));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 WalkPlan walk_plan(int S, int B, int64_t vocab) {
   WalkPlan p;

@@ -54,7 +54,8 @@ typedef enum {
   DDT_ERR_INVALID_ARG = -1,
   DDT_ERR_UNSUPPORTED = -2,
   DDT_ERR_WORKSPACE = -3,
-  DDT_ERR_HIP = -4
+  DDT_ERR_HIP = -4,
+  DDT_ERR_TOO_LARGE = -5
 } ddt_status;
 
 typedef enum { DDT_F32 = 0, DDT_BF16 = 1 } ddt_dtype;
@@ -230,6 +231,28 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                   const float* target_logits, int S, int B, int L, int64_t vocab,
                   int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok, int32_t* bonus_out,
                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- step 5, no allocation
+ * ddt_tree_walk without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, outputs and errors are those of ddt_tree_walk; the kernels
+ * are the same.  Its workspace is a static device array of the library,
+ * ddt_tree_walk_noalloc_max_bytes() = 1 MiB, of which a call needs
+ * ddt_tree_walk_workspace_size(S, B, vocab) bytes (256-byte-rounded 4 bytes per
+ * sequence, then 4 + 8 bytes per node row: S * (B + 1) rows up to about 87000).  A
+ * larger problem returns DDT_ERR_TOO_LARGE before any launch.
+ * Each GPU the library runs on holds its own copy of the array until the process
+ * ends.  The first call on a device looks up the array's address there and enqueues
+ * a zero fill of it on `stream` ahead of the walk; every walk leaves the part it used
+ * zero-filled again.  All calls on one GPU share that array: calls that may overlap
+ * on one GPU (different streams, or concurrently replayed graphs) race and must be
+ * ordered by the caller.  The call allocates nothing: no hipMalloc, no hipFree.
+ */
+size_t ddt_tree_walk_noalloc_max_bytes(void);
+int ddt_tree_walk_noalloc(const int32_t* tree_tok, const int32_t* parent, const int32_t* num_nodes,
+                          const float* target_logits, int S, int B, int L, int64_t vocab,
+                          int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok,
+                          int32_t* bonus_out, void* stream);
 
 /* ---------------------------------------------------------------- benchmark aid
  * Timing of the attention step (the round's dominant cost) with HIP events on the

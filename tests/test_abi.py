@@ -130,6 +130,22 @@ def test_walk_validation():
     assert call(ws_bytes=lib.ddt_tree_walk_workspace_size(1, 8, 64) - 1) == -3
 
 
+def test_walk_noalloc_validation():
+    """The allocation-free walk rejects a problem whose workspace exceeds its static
+    scratch (1 MiB) before any launch, and validates like ddt_tree_walk."""
+    lib = ddt.load()
+    a = [_fake(i) for i in range(1, 12)]
+
+    def call(S=1, B=8, L=4, V=64, tt=a[0]):
+        return lib.ddt_tree_walk_noalloc(tt, a[1], a[2], a[3], S, B, L, V, a[4], a[5], a[6], a[7], None)
+    assert lib.ddt_tree_walk_noalloc_max_bytes() == 1 << 20
+    assert call(tt=None) == -1
+    assert call(L=65) == -1
+    assert call(S=100, B=1023, V=1000) == -5      # 102400 rows: 1.2 MB of keys and counters
+    assert lib.ddt_tree_walk_workspace_size(100, 1023, 1000) > lib.ddt_tree_walk_noalloc_max_bytes()
+    assert lib.ddt_status_string(-5) == b"problem larger than the library's static scratch"
+
+
 def test_product_path_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libddt.so")
