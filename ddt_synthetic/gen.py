@@ -198,3 +198,89 @@ def batch(cfg: Config, attempts: Optional[Sequence[int]] = None,
                 fill(s)
         out.update(q=q, k_cache=kc, v_cache=vc, k_tree=kt, v_tree=vt)
     return out
+
+
+# ----------------------------------------------------------------------------- several rounds
+# A synthetic model keyed by the whole generated sequence, for loops of verification
+# rounds (the DDTree page, section 運作流程: each round starts from the bonus token the
+# previous one emitted, and the target's output carries over from round to round).
+# ``g`` is the list of generated tokens of a sequence: the first bonus token b_0 and
+# every token emitted after it; the initial context (the prefix) is fixed per
+# sequence.  Everything below is drawn from seeds keyed by (workload, sequence, tag,
+# *g), so each quantity is a function of its context, as a real model's would be:
+#   planted_next(g)   the target's planted next token after g (uniform draw)
+#   seq_target_row(g) target logits after g: N(0, 1) noise plus 10 on planted_next(g)
+#   seq_draft(g)      a round's draft logits [L, V] from context g (g ends with the
+#                     round's bonus token): N(0, 2^2) noise; position i's planted token
+#                     is the target's i-th planted continuation c_i (c_1 =
+#                     planted_next(g), c_{i+1} = planted_next(g + c_1..c_i)) with
+#                     probability 0.85, else a uniform token, lifted by 6 - 0.4 i plus
+#                     cfg.chain_boost.  ``attempt`` re-draws the noise and the errors.
+#   seq_node_qkv(g)   Q [Hq, D], K and V [Hkv, D] of the last token of g in context
+_T_SEQ_FIRST, _T_SEQ_NEXT, _T_SEQ_TARGET, _T_SEQ_DRAFT, _T_SEQ_ERR, _T_SEQ_QKV = 20, 21, 22, 23, 24, 25
+DRAFT_HIT_PROB = 0.85
+
+
+def seq_first_bonus(cfg: Config, seq: int) -> int:
+    """b_0: the bonus token the first round starts from."""
+    return int(_rng(cfg.cfg_id, seq, _T_SEQ_FIRST).integers(0, cfg.V))
+
+
+def planted_next(cfg: Config, seq: int, g: Sequence[int]) -> int:
+    return int(_rng(cfg.cfg_id, seq, _T_SEQ_NEXT, *[int(t) for t in g]).integers(0, cfg.V))
+
+
+def seq_target_row(cfg: Config, seq: int, g: Sequence[int]) -> np.ndarray:
+    """The synthetic target's next-token logits [V] fp32 after generated tokens g."""
+    r = _rng(cfg.cfg_id, seq, _T_SEQ_TARGET, *[int(t) for t in g])
+    row = r.standard_normal(cfg.V, dtype=np.float32)
+    t = planted_next(cfg, seq, g)
+    row[t] = np.float32(np.float64(row[t]) + TARGET_BOOST)
+    return row
+
+
+def seq_draft(cfg: Config, seq: int, g: Sequence[int], attempt: int = 0) -> np.ndarray:
+    """Draft logits [L, V] fp32 of a round whose context is g (ending in its bonus)."""
+    key = [int(t) for t in g]
+    r = _rng(cfg.cfg_id, seq, _T_SEQ_DRAFT, attempt, *key)
+    logits = (np.float32(2.0) * r.standard_normal((cfg.L, cfg.V), dtype=np.float32)).astype(np.float32)
+    e = _rng(cfg.cfg_id, seq, _T_SEQ_ERR, attempt, *key)
+    hit = e.random(cfg.L) < DRAFT_HIT_PROB
+    wrong = e.integers(0, cfg.V, size=cfg.L)
+    ctx = list(key)
+    for i in range(1, cfg.L + 1):
+        c = planted_next(cfg, seq, ctx)
+        t = c if hit[i - 1] else int(wrong[i - 1])
+        logits[i - 1, t] = np.float32(np.float64(logits[i - 1, t]) + (6.0 - 0.4 * i) + cfg.chain_boost)
+        ctx.append(c)
+    return logits
+
+
+def seq_node_qkv(cfg: Config, seq: int, g: Sequence[int]) -> Dict[str, np.ndarray]:
+    """Q [Hq, D] and K, V [Hkv, D] of the last token of g (bf16 encodings for the bf16
+    workloads, fp32 otherwise)."""
+    r = _rng(cfg.cfg_id, seq, _T_SEQ_QKV, *[int(t) for t in g])
+    out = {}
+    for name, shp in (("q", (cfg.Hq, cfg.D)), ("k", (cfg.Hkv, cfg.D)), ("v", (cfg.Hkv, cfg.D))):
+        x = r.standard_normal(shp, dtype=np.float32)
+        out[name] = f32_to_bf16_bits(x) if cfg.dtype == "bf16" else x
+    return out
+
+
+def seq_tree_inputs(cfg: Config, seq: int, g: Sequence[int], tree_tok: np.ndarray,
+                    parent: np.ndarray, num_nodes: int) -> Dict[str, np.ndarray]:
+    """A round's verifier inputs at a tree whose root is the last token of g: Q
+    [N,Hq,D], tree K/V [N,Hkv,D] and target logits [N,V] of every node, each from the
+    node's context g + (its path); rows past num_nodes are zero."""
+    et = np.uint16 if cfg.dtype == "bf16" else np.float32
+    q = np.zeros((cfg.N, cfg.Hq, cfg.D), dtype=et)
+    kt = np.zeros((cfg.N, cfg.Hkv, cfg.D), dtype=et)
+    vt = np.zeros_like(kt)
+    tl = np.zeros((cfg.N, cfg.V), dtype=np.float32)
+    base = [int(t) for t in g]
+    for n, path in enumerate(node_paths(tree_tok, parent, num_nodes)):
+        ctx = base + list(path)
+        x = seq_node_qkv(cfg, seq, ctx)
+        q[n], kt[n], vt[n] = x["q"], x["k"], x["v"]
+        tl[n] = seq_target_row(cfg, seq, ctx)
+    return {"q": q, "k_tree": kt, "v_tree": vt, "target": tl}

@@ -9,3 +9,4 @@ from .ddtree import (  # noqa: F401
     topk, tree_attention, tree_mask, tree_walk, visible_nodes,
 )
 from .round import verify_round  # noqa: F401
+from .rounds import commit_kv, greedy_decode, run_rounds  # noqa: F401
