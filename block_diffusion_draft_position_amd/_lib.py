@@ -42,13 +42,14 @@ def load() -> ctypes.CDLL:
         "ddt_topk_workspace_size": (sz, [i64, i64, i32]),
         "ddt_topk": (i32, [vp, i64, i64, i64, i32, vp, vp, vp, sz, vp]),
         "ddt_build_tree": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
-        "ddt_tree_mask": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp]),
+        "ddt_tree_mask": (i32, [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp]),
         "ddt_draft_tree_workspace_size": (sz, [i32, i32, i64, i32]),
-        "ddt_draft_tree": (i32, [vp, i64, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp, vp,
-                                 vp, vp, vp, vp, sz, vp]),
+        "ddt_draft_tree": (i32, [vp, i64, vp, vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, vp,
+                                 vp, vp, vp, vp, vp, sz, vp]),
         "ddt_tree_attention_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i64]),
-        "ddt_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                     f32, i64, vp, vp, vp, sz, vp]),
+        "ddt_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     i32, f32, i64, vp, vp, vp, sz, vp]),
+        "ddt_commit_kv": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]),
         "ddt_tree_walk_workspace_size": (sz, [i32, i32, i64]),
         "ddt_tree_walk": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]),
         "ddt_tree_walk_noalloc_max_bytes": (sz, []),
@@ -67,7 +68,7 @@ def load() -> ctypes.CDLL:
 
 EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_build_tree",
            "ddt_tree_mask", "ddt_draft_tree_workspace_size", "ddt_draft_tree",
-           "ddt_tree_attention_workspace_size", "ddt_tree_attention",
+           "ddt_tree_attention_workspace_size", "ddt_tree_attention", "ddt_commit_kv",
            "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_tree_walk_noalloc_max_bytes",
            "ddt_tree_walk_noalloc", "ddt_attention_profiling", "ddt_attention_timing")
 
@@ -141,8 +142,14 @@ def ddt_build_tree(topk_tok: torch.Tensor, topk_logq: torch.Tensor, bonus: torch
     return out
 
 
+def _prefix_len(prefix_len, S):
+    if prefix_len is not None:
+        _dev(prefix_len, "prefix_len", torch.int64, (S,))
+    return prefix_len
+
+
 def ddt_tree_mask(parent: torch.Tensor, depth: torch.Tensor, num_nodes: torch.Tensor,
-                  cu_prefix: Optional[torch.Tensor], mask=None, pos_ids=None):
+                  cu_prefix: Optional[torch.Tensor], mask=None, pos_ids=None, prefix_len=None):
     """-> (mask [S,N,W] int32 view of uint32 bits, pos_ids [S,N] or None)."""
     lib = load()
     S, N = parent.shape
@@ -157,13 +164,15 @@ def ddt_tree_mask(parent: torch.Tensor, depth: torch.Tensor, num_nodes: torch.Te
         mask = torch.empty(S, N, W, dtype=torch.int32, device=dev)
     if pos_ids is None and cu_prefix is not None:
         pos_ids = torch.empty(S, N, dtype=torch.int32, device=dev)
-    _check(lib.ddt_tree_mask(_p(parent), _p(depth), _p(num_nodes), _p(cu_prefix), S, N - 1,
-                             _p(mask), _p(pos_ids), _stream(dev)), "ddt_tree_mask")
+    _prefix_len(prefix_len, S)
+    _check(lib.ddt_tree_mask(_p(parent), _p(depth), _p(num_nodes), _p(cu_prefix), _p(prefix_len),
+                             S, N - 1, _p(mask), _p(pos_ids), _stream(dev)), "ddt_tree_mask")
     return mask, pos_ids
 
 
 def ddt_draft_tree(logits: torch.Tensor, bonus: torch.Tensor, cu_prefix: Optional[torch.Tensor],
-                   K: int, B: int, out: Optional[Dict[str, torch.Tensor]] = None, ws=None):
+                   K: int, B: int, out: Optional[Dict[str, torch.Tensor]] = None, ws=None,
+                   prefix_len=None):
     """logits [S,L,V] fp32, bonus [S], cu_prefix [S+1] or None -> dict with topk_tok,
     topk_logq, tree_tok, parent, depth, node_logq, num_nodes, mask (int32 view of
     uint32 bits) and pos_ids (None without cu_prefix): steps 1-3 in two launches."""
@@ -188,7 +197,8 @@ def ddt_draft_tree(logits: torch.Tensor, bonus: torch.Tensor, cu_prefix: Optiona
     need = lib.ddt_draft_tree_workspace_size(S, L, V, K)
     if ws is None:
         ws = _ws(need, dev)
-    _check(lib.ddt_draft_tree(_p(logits), V, _p(bonus), _p(cu_prefix), S, L, V, K, B,
+    _prefix_len(prefix_len, S)
+    _check(lib.ddt_draft_tree(_p(logits), V, _p(bonus), _p(cu_prefix), _p(prefix_len), S, L, V, K, B,
                               _p(out.get("topk_tok")), _p(out.get("topk_logq")),
                               _p(out["tree_tok"]), _p(out["parent"]), _p(out["depth"]),
                               _p(out.get("node_logq")), _p(out["num_nodes"]), _p(out["mask"]),
@@ -203,7 +213,7 @@ def attention_workspace_size(S, B, Hq, Hkv, D, dtype, max_prefix) -> int:
 
 def ddt_tree_attention(q, k_cache, v_cache, cu_prefix, k_tree, v_tree, mask, num_nodes,
                        scale: Optional[float] = None, max_prefix: Optional[int] = None,
-                       with_lse: bool = True, out=None, lse=None, ws=None):
+                       with_lse: bool = True, out=None, lse=None, ws=None, prefix_len=None):
     """q [S,N,Hq,D]; k/v_cache [T,Hkv,D]; k/v_tree [S,N,Hkv,D] (fp32 or bf16) ->
     (out [S,N,Hq,D], lse [S,N,Hq] fp32 or None)."""
     lib = load()
@@ -224,9 +234,11 @@ def ddt_tree_attention(q, k_cache, v_cache, cu_prefix, k_tree, v_tree, mask, num
     _dev(num_nodes, "num_nodes", torch.int32, (S,))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    _prefix_len(prefix_len, S)
     if max_prefix is None:
         cu = cu_prefix.cpu()
-        max_prefix = int((cu[1:] - cu[:-1]).max())
+        lens = prefix_len.cpu() if prefix_len is not None else cu[1:] - cu[:-1]
+        max_prefix = int(lens.max())
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -235,11 +247,38 @@ def ddt_tree_attention(q, k_cache, v_cache, cu_prefix, k_tree, v_tree, mask, num
     need = lib.ddt_tree_attention_workspace_size(S, N - 1, Hq, Hkv, D, dt, max_prefix)
     if ws is None:
         ws = _ws(need, dev)
-    _check(lib.ddt_tree_attention(_p(q), _p(k_cache), _p(v_cache), _p(cu_prefix), _p(k_tree),
+    _check(lib.ddt_tree_attention(_p(q), _p(k_cache), _p(v_cache), _p(cu_prefix), _p(prefix_len), _p(k_tree),
                                   _p(v_tree), _p(mask), _p(num_nodes), S, N - 1, Hq, Hkv, D, dt,
                                   float(scale), int(max_prefix), _p(out), _p(lse if with_lse else None),
                                   _p(ws), ws.numel(), _stream(dev)), "ddt_tree_attention")
     return out, (lse if with_lse else None)
+
+
+def ddt_commit_kv(k_cache, v_cache, cu_prefix, prefix_len, k_tree, v_tree, acc_nodes, accept_len,
+                  appended=None):
+    """Append each sequence's root and accepted nodes' tree K/V to its cache region
+    and advance prefix_len, in place; returns appended [S] int32 (-1: no room)."""
+    lib = load()
+    S, N, Hkv, D = k_tree.shape
+    dt = {torch.float32: DDT_F32, torch.bfloat16: DDT_BF16}.get(k_tree.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {k_tree.dtype}")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("v_tree", v_tree)):
+        _dev(t, name, k_tree.dtype)
+    if k_cache.shape != v_cache.shape or tuple(k_cache.shape[1:]) != (Hkv, D):
+        raise ValueError("k_cache/v_cache must be [rows, Hkv, D]")
+    _dev(v_tree, "v_tree", k_tree.dtype, (S, N, Hkv, D))
+    _dev(cu_prefix, "cu_prefix", torch.int64, (S + 1,))
+    _dev(prefix_len, "prefix_len", torch.int64, (S,))
+    _dev(accept_len, "accept_len", torch.int32, (S,))
+    _dev(acc_nodes, "acc_nodes", torch.int32)
+    L = acc_nodes.shape[1]
+    if appended is None:
+        appended = torch.empty(S, dtype=torch.int32, device=k_tree.device)
+    _check(lib.ddt_commit_kv(_p(k_cache), _p(v_cache), _p(cu_prefix), _p(prefix_len), _p(k_tree),
+                             _p(v_tree), _p(acc_nodes), _p(accept_len), S, N - 1, L, Hkv, D, dt,
+                             _p(appended), _stream(k_tree.device)), "ddt_commit_kv")
+    return appended
 
 
 def ddt_tree_walk(tree_tok, parent, num_nodes, target_logits, L: int, out=None, ws=None):

@@ -126,12 +126,12 @@ int ddt_build_tree(const int32_t* topk_tok, const float* topk_logq, const int32_
 
 // ------------------------------------------------------------------ mask
 int ddt_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* num_nodes,
-                  const int64_t* cu_prefix, int S, int B, uint32_t* mask, int32_t* pos_ids,
-                  void* stream) {
+                  const int64_t* cu_prefix, const int64_t* prefix_len, int S, int B,
+                  uint32_t* mask, int32_t* pos_ids, void* stream) {
   if (!parent || !depth || !num_nodes || !mask) return DDT_ERR_INVALID_ARG;
   if (S < 1 || B < 0 || B > DDT_MAX_B) return DDT_ERR_INVALID_ARG;
-  return hip_status(launch_tree_mask(parent, depth, num_nodes, cu_prefix, S, B, mask, pos_ids,
-                                     as_stream(stream)));
+  return hip_status(launch_tree_mask(parent, depth, num_nodes, Prefix{cu_prefix, prefix_len}, S, B,
+                                     mask, pos_ids, as_stream(stream)));
 }
 
 // ------------------------------------------------------------------ steps 1-3 fused
@@ -141,7 +141,8 @@ size_t ddt_draft_tree_workspace_size(int S, int L, int64_t vocab, int K) {
 }
 
 int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus,
-                   const int64_t* cu_prefix, int S, int L, int64_t vocab, int K, int B,
+                   const int64_t* cu_prefix, const int64_t* prefix_len, int S, int L,
+                   int64_t vocab, int K, int B,
                    int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
                    int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
                    int32_t* pos_ids, void* ws, size_t ws_bytes, void* stream) {
@@ -158,9 +159,9 @@ int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus
   const hipStream_t st = as_stream(stream);
   hipError_t e = launch_topk_partial(logits, rows, vocab, row_stride, K, ws, plan, st);
   if (e != hipSuccess) return DDT_ERR_HIP;
-  return hip_status(launch_draft_tree(ws, plan, bonus, cu_prefix, S, L, K, B, topk_tok, topk_logq,
-                                      tree_tok, parent, depth, node_logq, num_nodes, mask,
-                                      cu_prefix ? pos_ids : nullptr, st));
+  return hip_status(launch_draft_tree(ws, plan, bonus, Prefix{cu_prefix, prefix_len}, S, L, K, B,
+                                      topk_tok, topk_logq, tree_tok, parent, depth, node_logq,
+                                      num_nodes, mask, cu_prefix ? pos_ids : nullptr, st));
 }
 
 // ------------------------------------------------------------------ attention
@@ -180,7 +181,8 @@ size_t ddt_tree_attention_workspace_size(int S, int B, int Hq, int Hkv, int D, i
 }
 
 int ddt_tree_attention(const void* q, const void* k_cache, const void* v_cache,
-                       const int64_t* cu_prefix, const void* k_tree, const void* v_tree,
+                       const int64_t* cu_prefix, const int64_t* prefix_len,
+                       const void* k_tree, const void* v_tree,
                        const uint32_t* mask, const int32_t* num_nodes, int S, int B, int Hq,
                        int Hkv, int D, int dtype, float scale, int64_t max_prefix, void* out,
                        float* lse, void* ws, size_t ws_bytes, void* stream) {
@@ -195,9 +197,30 @@ int ddt_tree_attention(const void* q, const void* k_cache, const void* v_cache,
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return DDT_ERR_WORKSPACE;
   if ((int64_t)S * Hkv * (plan.nsplit + 1) * plan.row_groups + 8 * (int64_t)plan.row_groups > INT32_MAX)
     return DDT_ERR_UNSUPPORTED;
-  return hip_status(launch_tree_attention(q, k_cache, v_cache, cu_prefix, k_tree, v_tree, mask,
+  return hip_status(launch_tree_attention(q, k_cache, v_cache, Prefix{cu_prefix, prefix_len},
+                                          k_tree, v_tree, mask,
                                           num_nodes, S, B, Hq, Hkv, D, scale, out, lse, ws, plan,
                                           as_stream(stream)));
+}
+
+// ------------------------------------------------------------------ KV commit
+int ddt_commit_kv(void* k_cache, void* v_cache, const int64_t* cu_prefix, int64_t* prefix_len,
+                  const void* k_tree, const void* v_tree, const int32_t* acc_nodes,
+                  const int32_t* accept_len, int S, int B, int L, int Hkv, int D, int dtype,
+                  int32_t* appended, void* stream) {
+  if (!k_cache || !v_cache || !cu_prefix || !prefix_len || !k_tree || !v_tree || !acc_nodes ||
+      !accept_len)
+    return DDT_ERR_INVALID_ARG;
+  if (S < 1 || B < 0 || B > DDT_MAX_B || L < 1 || L > DDT_MAX_L || Hkv < 1) return DDT_ERR_INVALID_ARG;
+  if (D != 32 && D != 64 && D != 128) return DDT_ERR_UNSUPPORTED;
+  if (dtype != DDT_F32 && dtype != DDT_BF16) return DDT_ERR_UNSUPPORTED;
+  for (const void* p : {(const void*)k_cache, (const void*)v_cache, k_tree, v_tree})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return DDT_ERR_INVALID_ARG;
+  const int64_t row_bytes = (int64_t)Hkv * D * (dtype == DDT_BF16 ? 2 : 4);
+  if (row_bytes / 16 > INT32_MAX / (DDT_MAX_L + 1)) return DDT_ERR_UNSUPPORTED;
+  return hip_status(launch_commit_kv(k_cache, v_cache, cu_prefix, prefix_len, k_tree, v_tree,
+                                     acc_nodes, accept_len, S, B + 1, L, row_bytes, appended,
+                                     as_stream(stream)));
 }
 
 // ------------------------------------------------------------------ walk

@@ -129,6 +129,19 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   argmax_step<32>(v, i);
 }
 
+// ---------------------------------------------------------------- prefix layout
+// Sequence s's prefix keys are cache rows cu[s] .. cu[s] + length(s); the length is
+// len[s] when given (rows up to cu[s + 1] are then capacity for appends), else
+// cu[s + 1] - cu[s].  A null cu means no prefix at all.
+struct Prefix {
+  const int64_t* cu;
+  const int64_t* len;
+  __device__ __forceinline__ int64_t start(int s) const { return cu ? cu[s] : 0; }
+  __device__ __forceinline__ int64_t length(int s) const {
+    return !cu ? 0 : len ? len[s] : cu[s + 1] - cu[s];
+  }
+};
+
 // ---------------------------------------------------------------- device properties
 int cu_count();  // compute units of the current device (cached per device)
 
@@ -165,7 +178,7 @@ hipError_t launch_build_tree(const int32_t* tok, const float* logq, const int32_
 // launch_topk_partial left in ws: one launch when a workgroup can give every draft
 // position its own merge wave (draft_tree_uses_fused), else the three kernels.
 hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t* bonus,
-                             const int64_t* cu_prefix, int S, int L, int K, int B,
+                             Prefix pre, int S, int L, int K, int B,
                              int32_t* topk_tok, float* topk_logq, int32_t* tree_tok,
                              int32_t* parent, int32_t* depth, float* node_logq,
                              int32_t* num_nodes, uint32_t* mask, int32_t* pos_ids,
@@ -174,7 +187,7 @@ bool draft_tree_uses_fused(int L, int K, int B, const TopkPlan& plan);
 
 // mask
 hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* num_nodes,
-                            const int64_t* cu_prefix, int S, int B, uint32_t* mask,
+                            Prefix pre, int S, int B, uint32_t* mask,
                             int32_t* pos_ids, hipStream_t st);
 
 // attention
@@ -189,7 +202,7 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_prefix);
 hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
-                                 const int64_t* cu_prefix, const void* kt, const void* vt,
+                                 Prefix pre, const void* kt, const void* vt,
                                  const uint32_t* mask, const int32_t* num_nodes, int S, int B,
                                  int Hq, int Hkv, int D, float scale, void* out, float* lse,
                                  void* ws, const AttnPlan& plan, hipStream_t st);
@@ -214,6 +227,13 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,
                             int32_t* acc_tok, int32_t* bonus_out, void* ws, const WalkPlan& plan,
                             hipStream_t st);
+
+// KV commit: appends each sequence's root and accepted nodes' tree K/V rows to its
+// cache region and advances prefix_len (one workgroup per sequence).
+hipError_t launch_commit_kv(void* k_cache, void* v_cache, const int64_t* cu_prefix,
+                            int64_t* prefix_len, const void* k_tree, const void* v_tree,
+                            const int32_t* acc_nodes, const int32_t* accept_len, int S, int N,
+                            int L, int64_t row_bytes, int32_t* appended, hipStream_t st);
 
 // Benchmark timing of the attention's main kernel and of the whole attention step
 // (see ddt_attention_profiling).  While profiling is on, prof_events hands out a

@@ -28,7 +28,7 @@ template <int J, int SK, int ME>
 __global__ void __launch_bounds__(waves_for(J, ME) * kWave)
 draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __restrict__ stats,
                   int nchunks, const int32_t* __restrict__ bonus,
-                  const int64_t* __restrict__ cu_prefix, int L, int K, int B,
+                  Prefix pre, int L, int K, int B,
                   int32_t* __restrict__ topk_tok, float* __restrict__ topk_logq,
                   int32_t* __restrict__ tree_tok, int32_t* __restrict__ tree_parent,
                   int32_t* __restrict__ tree_depth, float* __restrict__ node_logq,
@@ -48,7 +48,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
   tree::TreeSmem sm = tree::carve(smem_raw + NW * sizeof(topk::WaveLds), N, LK);
   // the builder's scalars, requested now so they arrive during the merge
   const int bonus_tok = bonus[s];
-  const int P = (pos_ids && cu_prefix) ? (int)(cu_prefix[s + 1] - cu_prefix[s]) : 0;
+  const int P = (pos_ids && pre.cu) ? (int)pre.length(s) : 0;
 
   for (int i = threadIdx.x; i < DDT_MAX_L; i += NW * kWave) ready[i] = 0;
   __syncthreads();
@@ -74,7 +74,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
     const int64_t o = (int64_t)s * N;
     const int n = tree::build<J, SK>(sm, L, K, B, bonus_tok, tree_tok + o, tree_parent + o,
                                      tree_depth + o, node_logq ? node_logq + o : nullptr,
-                                     (pos_ids && cu_prefix) ? pos_ids + o : nullptr, P,
+                                     (pos_ids && pre.cu) ? pos_ids + o : nullptr, P,
                                      [] { topk::wave_lds_sync(); },
                                      [&](int m) {
                                        for (;;) {
@@ -98,7 +98,7 @@ draft_tree_kernel(const unsigned long long* __restrict__ cand, const float2* __r
 
 template <int J, int SK, int ME>
 hipError_t launch_jkm(const unsigned long long* cand, const float2* stats, int nchunks,
-                      const int32_t* bonus, const int64_t* cu_prefix, int S, int L, int K, int B,
+                      const int32_t* bonus, Prefix pre, int S, int L, int K, int B,
                       int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
                       int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
                       int32_t* pos_ids, hipStream_t st) {
@@ -111,19 +111,19 @@ hipError_t launch_jkm(const unsigned long long* cand, const float2* stats, int n
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((draft_tree_kernel<J, SK, ME>), dim3(S), dim3(NW * kWave), smem, st, cand,
-                     stats, nchunks, bonus, cu_prefix, L, K, B, topk_tok, topk_logq, tree_tok,
+                     stats, nchunks, bonus, pre, L, K, B, topk_tok, topk_logq, tree_tok,
                      parent, depth, node_logq, num_nodes, mask, pos_ids);
   return hipGetLastError();
 }
 
 template <int J, int ME>
 hipError_t launch_jm(int K, const unsigned long long* cand, const float2* stats, int nchunks,
-                     const int32_t* bonus, const int64_t* cu_prefix, int S, int L, int B,
+                     const int32_t* bonus, Prefix pre, int S, int L, int B,
                      int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
                      int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
                      int32_t* pos_ids, hipStream_t st) {
 #define DDT_ARGS_SK                                                                         \
-  cand, stats, nchunks, bonus, cu_prefix, S, L, K, B, topk_tok, topk_logq, tree_tok, parent, \
+  cand, stats, nchunks, bonus, pre, S, L, K, B, topk_tok, topk_logq, tree_tok, parent, \
       depth, node_logq, num_nodes, mask, pos_ids, st
   if constexpr (J <= 2) {
     if (K <= 8) return launch_jkm<J, 8, ME>(DDT_ARGS_SK);
@@ -148,7 +148,7 @@ bool draft_tree_uses_fused(int L, int K, int B, const TopkPlan& plan) {
 }
 
 hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t* bonus,
-                             const int64_t* cu_prefix, int S, int L, int K, int B,
+                             Prefix pre, int S, int L, int K, int B,
                              int32_t* topk_tok, float* topk_logq, int32_t* tree_tok,
                              int32_t* parent, int32_t* depth, float* node_logq,
                              int32_t* num_nodes, uint32_t* mask, int32_t* pos_ids,
@@ -161,14 +161,14 @@ hipError_t launch_draft_tree(const void* ws, const TopkPlan& plan, const int32_t
     e = launch_build_tree(topk_tok, topk_logq, bonus, S, L, K, B, tree_tok, parent, depth,
                           node_logq, num_nodes, st);
     if (e != hipSuccess) return e;
-    return launch_tree_mask(parent, depth, num_nodes, cu_prefix, S, B, mask, pos_ids, st);
+    return launch_tree_mask(parent, depth, num_nodes, pre, S, B, mask, pos_ids, st);
   }
   unsigned long long* cand;
   float2* stats;
   topk_ws_parts(const_cast<void*>(ws), (int64_t)S * L, K, plan, &cand, &stats);
   const int slots = slots_for(B);
 #define DDT_ARGS                                                                               \
-  K, cand, stats, plan.nchunks, bonus, cu_prefix, S, L, B, topk_tok, topk_logq, tree_tok, parent, \
+  K, cand, stats, plan.nchunks, bonus, pre, S, L, B, topk_tok, topk_logq, tree_tok, parent, \
       depth, node_logq, num_nodes, mask, pos_ids, st
 #define DDT_J(JJ)                                                              \
   return plan.merge_e == 8 ? launch_jm<JJ, 8>(DDT_ARGS)    \

@@ -93,7 +93,7 @@ __device__ __forceinline__ bool decode_block(int Hkv, int nsplit_tot, int row_gr
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64)
 attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-                  const bf16_t* __restrict__ vc, const int64_t* __restrict__ cu_prefix,
+                  const bf16_t* __restrict__ vc, Prefix pre,
                   const bf16_t* __restrict__ kt, const bf16_t* __restrict__ vt,
                   const uint32_t* __restrict__ mask, const int32_t* __restrict__ num_nodes,
                   int N, int Hq, int Hkv, int G, int R, int W, int rows_pad, int nsplit,
@@ -122,8 +122,8 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int l32 = lane % 32;
 
   const int nn = num_nodes[u.s];
-  const int64_t p0 = cu_prefix[u.s];
-  const int64_t P = kc ? cu_prefix[u.s + 1] - p0 : 0;
+  const int64_t p0 = pre.start(u.s);
+  const int64_t P = kc ? pre.length(u.s) : 0;
   const int64_t kstride = (int64_t)Hkv * D;   // elements between consecutive keys
   const bool tree = u.c == nsplit;
   int64_t lo, hi;
@@ -380,7 +380,7 @@ __device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >>
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, NW <= 4 ? 2 : 1)
 attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-          const bf16_t* __restrict__ vc, const int64_t* __restrict__ cu_prefix,
+          const bf16_t* __restrict__ vc, Prefix pre,
           const bf16_t* __restrict__ kt, const bf16_t* __restrict__ vt,
           const uint32_t* __restrict__ mask, const int32_t* __restrict__ num_nodes,
           int N, int Hq, int Hkv, int G, int R, int W, int rows_pad, int nsplit,
@@ -401,8 +401,8 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const bool live = (u.rg * NW + wave) * 32 < R;
 
   const int nn = num_nodes[u.s];
-  const int64_t p0 = cu_prefix[u.s];
-  const int64_t P = kc ? cu_prefix[u.s + 1] - p0 : 0;
+  const int64_t p0 = pre.start(u.s);
+  const int64_t P = kc ? pre.length(u.s) : 0;
   const int64_t kstride = (int64_t)Hkv * D;
   const bool tree = u.c == nsplit;
   int64_t lo, hi;
@@ -673,7 +673,7 @@ constexpr int kCombineThreads = 128;
 template <typename OutT, int D, int KB>
 __global__ void __launch_bounds__(kCombineThreads)
 attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
-             const int64_t* __restrict__ cu_prefix, const int32_t* __restrict__ num_nodes, int S,
+             Prefix pre, const int32_t* __restrict__ num_nodes, int S,
              int N, int Hq, int Hkv, int G, int rows_pad, int nsplit, int64_t chunk,
              bool has_cache, OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int TPR = D / 4;            // threads per row, 4 outputs each
@@ -693,7 +693,7 @@ attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
   }
   const int g = h / G;
   const int row = n * G + (h % G);
-  const int64_t P = has_cache ? cu_prefix[s + 1] - cu_prefix[s] : 0;
+  const int64_t P = has_cache ? pre.length(s) : 0;
   const int nvalid = P > 0 ? (int)min<int64_t>(nsplit, (P + chunk - 1) / chunk) : 0;
   const int64_t base = ((int64_t)s * Hkv + g) * (nsplit + 1);
   // the splits that hold keys: prefix splits 0 .. nvalid-1, then the tree split
@@ -742,7 +742,7 @@ attn_combine(const float* __restrict__ opart, const float2* __restrict__ mlpart,
 template <int D>
 __global__ void __launch_bounds__(64)
 attn_f32(const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
-         const int64_t* __restrict__ cu_prefix, const float* __restrict__ kt,
+         Prefix pre, const float* __restrict__ kt,
          const float* __restrict__ vt, const uint32_t* __restrict__ mask,
          const int32_t* __restrict__ num_nodes, int N, int Hq, int Hkv, int W, float scale,
          float* __restrict__ out, float* __restrict__ lse) {
@@ -763,8 +763,8 @@ attn_f32(const float* __restrict__ q, const float* __restrict__ kc, const float*
   const int g = h / (Hq / Hkv);
   for (int d = lane; d < D; d += 64) qs[d] = q[rid * D + d];
   __syncthreads();
-  const int64_t p0 = cu_prefix[s];
-  const int64_t P = kc ? cu_prefix[s + 1] - p0 : 0;
+  const int64_t p0 = pre.start(s);
+  const int64_t P = kc ? pre.length(s) : 0;
   float m = -INFINITY, l = 0.f;
   float acc[DPL];
 #pragma unroll
@@ -840,7 +840,7 @@ attn_f32(const float* __restrict__ q, const float* __restrict__ kc, const float*
 
 template <int D, int NW>
 hipError_t launch_partial(const AttnPlan& p, const void* q, const void* kc, const void* vc,
-                          const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
+                          Prefix cu, const void* kt, const void* vt, const uint32_t* mask,
                           const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
                           float* opart, float2* ml, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {
@@ -856,7 +856,7 @@ hipError_t launch_partial(const AttnPlan& p, const void* q, const void* kc, cons
 
 template <int NW>
 hipError_t launch_d128_nw(const AttnPlan& p, const void* q, const void* kc, const void* vc,
-                          const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
+                          Prefix cu, const void* kt, const void* vt, const uint32_t* mask,
                           const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
                           float* opart, float2* ml, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {
@@ -871,7 +871,7 @@ hipError_t launch_d128_nw(const AttnPlan& p, const void* q, const void* kc, cons
 }
 
 hipError_t launch_d128(const AttnPlan& p, const void* q, const void* kc, const void* vc,
-                       const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
+                       Prefix cu, const void* kt, const void* vt, const uint32_t* mask,
                        const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
                        float* opart, float2* ml, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
 #define DDT_NW(X)                                                                            \
@@ -888,7 +888,7 @@ hipError_t launch_d128(const AttnPlan& p, const void* q, const void* kc, const v
 
 template <int D>
 hipError_t launch_partial_d(const AttnPlan& p, const void* q, const void* kc, const void* vc,
-                            const int64_t* cu, const void* kt, const void* vt, const uint32_t* mask,
+                            Prefix cu, const void* kt, const void* vt, const uint32_t* mask,
                             const int32_t* nn, int S, int N, int Hq, int Hkv, int W, float scale,
                             float* opart, float2* ml, hipStream_t st, hipEvent_t ev0,
                             hipEvent_t ev1) {
@@ -969,7 +969,7 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_
 }
 
 hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
-                                 const int64_t* cu_prefix, const void* kt, const void* vt,
+                                 Prefix pre, const void* kt, const void* vt,
                                  const uint32_t* mask, const int32_t* num_nodes, int S, int B,
                                  int Hq, int Hkv, int D, float scale, void* out, float* lse,
                                  void* ws, const AttnPlan& p, hipStream_t st) {
@@ -982,7 +982,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
 #define DDT_F32_D(DD)                                                                          \
   case DD:                                                                                     \
     hipExtLaunchKernelGGL(attn_f32<DD>, dim3((unsigned)rows), dim3(64), 0, st, ev0, ev1, 0,    \
-                          (const float*)q, (const float*)kc, (const float*)vc, cu_prefix,      \
+                          (const float*)q, (const float*)kc, (const float*)vc, pre,            \
                           (const float*)kt, (const float*)vt, mask, num_nodes, N, Hq, Hkv, W,  \
                           scale, (float*)out, lse);                                            \
     return hipGetLastError();
@@ -1000,9 +1000,9 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   hipEvent_t ev0 = nullptr, ev1 = nullptr, ev2 = nullptr;
   if (!prof_events(&ev0, &ev1, &ev2)) ev0 = ev1 = ev2 = nullptr;
   switch (D) {
-    case 32: e = launch_partial_d<32>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
-    case 64: e = launch_partial_d<64>(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
-    case 128: e = launch_d128(p, q, kc, vc, cu_prefix, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
+    case 32: e = launch_partial_d<32>(p, q, kc, vc, pre, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
+    case 64: e = launch_partial_d<64>(p, q, kc, vc, pre, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
+    case 128: e = launch_d128(p, q, kc, vc, pre, kt, vt, mask, num_nodes, S, N, Hq, Hkv, W, scale, opart, ml, st, ev0, ev1); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
@@ -1014,7 +1014,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
   const int kb = nused <= 2 ? 2 : nused <= 4 ? 4 : nused <= 8 ? 8 : nused <= 16 ? 16 : 32;
 #define DDT_COMB_KB(DD, KK)                                                                     \
   hipExtLaunchKernelGGL((attn_combine<bf16_t, DD, KK>), dim3(blocks), dim3(kCombineThreads), 0, \
-                        st, nullptr, ev2, 0, opart, ml, cu_prefix, num_nodes, S, N, Hq, Hkv,    \
+                        st, nullptr, ev2, 0, opart, ml, pre, num_nodes, S, N, Hq, Hkv,          \
                         p.G, p.rows_pad, p.nsplit, p.chunk, kc != nullptr, (bf16_t*)out, lse)
 #define DDT_COMB(DD)                                     \
   case DD:                                               \

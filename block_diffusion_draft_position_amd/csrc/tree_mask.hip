@@ -17,7 +17,7 @@ constexpr int kPerThread = 1;  // items per thread in a slice (4: -0.75% rounds/
 
 __global__ void __launch_bounds__(kThreads)
 tree_mask_kernel(const int32_t* __restrict__ parent, const int32_t* __restrict__ depth,
-                 const int32_t* __restrict__ num_nodes, const int64_t* __restrict__ cu_prefix,
+                 const int32_t* __restrict__ num_nodes, Prefix pre,
                  int N, int W, int slices, uint32_t* __restrict__ mask,
                  int32_t* __restrict__ pos_ids) {
   extern __shared__ int par[];
@@ -31,7 +31,7 @@ tree_mask_kernel(const int32_t* __restrict__ parent, const int32_t* __restrict__
   mask::rows(par, nn, N, W, mask + (int64_t)s * N * W, threadIdx.x, kThreads, slice * per,
              min(N * W, (slice + 1) * per));
   if (pos_ids && slice == 0) {
-    const int32_t P = (int32_t)(cu_prefix[s + 1] - cu_prefix[s]);
+    const int32_t P = (int32_t)pre.length(s);
     for (int n = threadIdx.x; n < N; n += kThreads)
       pos_ids[(int64_t)s * N + n] = (n < nn) ? P + depth[(int64_t)s * N + n] : -1;
   }
@@ -40,13 +40,13 @@ tree_mask_kernel(const int32_t* __restrict__ parent, const int32_t* __restrict__
 }  // namespace
 
 hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* num_nodes,
-                            const int64_t* cu_prefix, int S, int B, uint32_t* mask,
+                            Prefix pre, int S, int B, uint32_t* mask,
                             int32_t* pos_ids, hipStream_t st) {
   const int N = B + 1;
   const int W = (N + 31) / 32;
   const int slices = (int)ceil_div(N * W, kThreads * kPerThread);
   hipLaunchKernelGGL(tree_mask_kernel, dim3(S * slices), dim3(kThreads), sizeof(int) * N, st, parent,
-                     depth, num_nodes, cu_prefix, N, W, slices, mask, cu_prefix ? pos_ids : nullptr);
+                     depth, num_nodes, pre, N, W, slices, mask, pre.cu ? pos_ids : nullptr);
   return hipGetLastError();
 }
 

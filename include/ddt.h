@@ -17,6 +17,9 @@
  * and ddt_draft_tree does the first three in two launches, with identical results.
  * (the target model's layers around the attention are the caller's).
  *
+ * Across rounds, ddt_commit_kv appends the accepted path's K/V to each sequence's cache
+ * and the walk's bonus token becomes the next round's root.
+ *
  * Conventions shared by every entry point
  *   - Array arguments are device pointers (hipMalloc'd or equivalent, visible to
  *     the current device); scalars are host values.  The caller owns every buffer.
@@ -34,6 +37,12 @@
  *   - Data preconditions, not checked: logits are finite; token ids are in
  *     [0, vocab); parent/depth arrays come from ddt_build_tree (or obey the same
  *     layout); cu_prefix is non-decreasing with cu_prefix[0] = 0.
+ *   - The prefix (context) of sequence s is described by cu_prefix [S+1] int64 and an
+ *     optional prefix_len [S] int64.  Without prefix_len, its P_s = cu_prefix[s+1] -
+ *     cu_prefix[s] keys are cache rows cu_prefix[s] .. cu_prefix[s+1] (sequences packed
+ *     back to back).  With prefix_len, they are rows cu_prefix[s] .. cu_prefix[s] +
+ *     prefix_len[s], and the rows up to cu_prefix[s+1] are room for ddt_commit_kv to
+ *     append to (0 <= prefix_len[s] <= cu_prefix[s+1] - cu_prefix[s]).
  *   - Tree arrays have N = B + 1 entries per sequence.  Node 0 is the root (the
  *     bonus token).  A sequence whose candidate tree holds fewer than B prefixes
  *     gets num_nodes < N; its trailing entries are padding (ids -1, logq -inf,
@@ -129,8 +138,9 @@ int ddt_build_tree(const int32_t* topk_tok, const float* topk_logq, const int32_
  * Compile the tree into the ancestor-only attention mask (核心創新; 運作流程 step 3).
  *
  * parent, depth  [S, N] as written by ddt_build_tree; num_nodes [S].
- * cu_prefix      nullable; [S+1] int64 prefix offsets (P_s = cu_prefix[s+1] -
- *                cu_prefix[s]).  When NULL, pos_ids is not written.
+ * cu_prefix      nullable; [S+1] int64 prefix offsets, with prefix_len (nullable) as
+ *                described above: they give P_s.  When cu_prefix is NULL, pos_ids is
+ *                not written.
  * mask           [S, N, W] uint32, W = ceil(N / 32): bit j of word j / 32 of row n
  *                is set iff node j is node n or one of its ancestors.  The prefix
  *                context is visible to every node and is not part of the mask.
@@ -140,8 +150,8 @@ int ddt_build_tree(const int32_t* topk_tok, const float* topk_logq, const int32_
  * Errors: null parent/depth/num_nodes/mask; S < 1; B outside [0, DDT_MAX_B].
  */
 int ddt_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* num_nodes,
-                  const int64_t* cu_prefix, int S, int B, uint32_t* mask, int32_t* pos_ids,
-                  void* stream);
+                  const int64_t* cu_prefix, const int64_t* prefix_len, int S, int B,
+                  uint32_t* mask, int32_t* pos_ids, void* stream);
 
 /* ---------------------------------------------------------------- steps 1-3 fused
  * ddt_topk, ddt_build_tree and ddt_tree_mask in two launches (a top-K pass over the
@@ -150,7 +160,8 @@ int ddt_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* nu
  *
  * logits      [S, L, vocab] fp32; row (s, i) at logits + (s * L + i) * row_stride;
  *             values as for ddt_topk.
- * bonus       [S]; cu_prefix nullable [S+1] (needed for pos_ids).
+ * bonus       [S]; cu_prefix nullable [S+1] and prefix_len nullable [S] (needed for
+ *             pos_ids; see the conventions above).
  * Limits as for the three calls: 1 <= L <= DDT_MAX_L, 1 <= K <= min(vocab,
  * DDT_MAX_K), 0 <= B <= DDT_MAX_B.
  * topk_tok, topk_logq [S, L, K]: the top-K step's outputs.
@@ -165,7 +176,8 @@ int ddt_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* nu
  */
 size_t ddt_draft_tree_workspace_size(int S, int L, int64_t vocab, int K);
 int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus,
-                   const int64_t* cu_prefix, int S, int L, int64_t vocab, int K, int B,
+                   const int64_t* cu_prefix, const int64_t* prefix_len, int S, int L,
+                   int64_t vocab, int K, int B,
                    int32_t* topk_tok, float* topk_logq, int32_t* tree_tok, int32_t* parent,
                    int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
                    int32_t* pos_ids, void* ws, size_t ws_bytes, void* stream);
@@ -175,14 +187,14 @@ int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus
  * under the ancestor-only mask (運作流程 step 3).
  *
  * For sequence s, node n < num_nodes[s] and query head h, with g = h / (Hq / Hkv):
- *   keys   = prefix K[cu_prefix[s] .. cu_prefix[s+1]) of KV head g, followed by
+ *   keys   = prefix K[cu_prefix[s] .. cu_prefix[s] + P_s) of KV head g, followed by
  *            k_tree[s, j, g] for every j visible in mask[s, n]
  *   out[s, n, h] = softmax(scale * q[s, n, h] . keys^T) . values
  *   lse[s, n, h] = natural log of sum exp(scale * q . k) over those keys
  * q          [S, N, Hq, D]                 (dtype)
- * k_cache,   [sum_s P_s, Hkv, D]           (dtype) sequences packed back to back
+ * k_cache,   [rows, Hkv, D]                (dtype) sequences back to back, cu_prefix[S] rows
  * v_cache
- * cu_prefix  [S+1] int64
+ * cu_prefix  [S+1] int64; prefix_len nullable [S] int64 (conventions above)
  * k_tree,    [S, N, Hkv, D]                (dtype) the tree nodes' own K/V
  * v_tree
  * mask       [S, N, W] from ddt_tree_mask; num_nodes [S]
@@ -199,11 +211,39 @@ int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus
 size_t ddt_tree_attention_workspace_size(int S, int B, int Hq, int Hkv, int D, int dtype,
                                          int64_t max_prefix);
 int ddt_tree_attention(const void* q, const void* k_cache, const void* v_cache,
-                       const int64_t* cu_prefix, const void* k_tree, const void* v_tree,
+                       const int64_t* cu_prefix, const int64_t* prefix_len,
+                       const void* k_tree, const void* v_tree,
                        const uint32_t* mask, const int32_t* num_nodes,
                        int S, int B, int Hq, int Hkv, int D, int dtype, float scale,
                        int64_t max_prefix, void* out, float* lse, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* ---------------------------------------------------------------- between rounds
+ * KV commit (運作流程: each round starts from a bonus token that the target produced
+ * but has not run forward, and the walk's first mismatch is carried into the next
+ * round as its bonus).  After the walk, the root and the accepted nodes n_1..n_a have
+ * been run through the target, each attending to exactly the prefix and its
+ * ancestors, which is their causal context in the continued sequence: their tree K/V
+ * rows, root first, become cache rows cu_prefix[s] + P_s .. cu_prefix[s] + P_s + a,
+ * and prefix_len[s] becomes P_s + a + 1.  The next round's root is the walk's
+ * bonus_out.
+ *
+ * k_cache, v_cache   [rows, Hkv, D] (dtype), written in place; 16-byte aligned.
+ * cu_prefix          [S+1]: sequence s owns rows cu_prefix[s] .. cu_prefix[s+1].
+ * prefix_len         [S] int64, read and advanced in place.
+ * k_tree, v_tree     [S, N, Hkv, D] (dtype) as given to ddt_tree_attention; 16-byte aligned.
+ * acc_nodes [S, L], accept_len [S]: from ddt_tree_walk.
+ * appended           nullable [S] int32: rows appended (a + 1), or -1 when the
+ *                    sequence's room cannot take them or its walk outputs are out of
+ *                    range; such a sequence's cache and prefix_len are left unchanged.
+ * 1 <= S, 0 <= B <= DDT_MAX_B, 1 <= L <= DDT_MAX_L, Hkv >= 1, D in {32, 64, 128}.
+ * Errors: null required pointer, unaligned cache or tree pointer, size out of range
+ *         (DDT_ERR_INVALID_ARG); D or dtype without a kernel (DDT_ERR_UNSUPPORTED).
+ */
+int ddt_commit_kv(void* k_cache, void* v_cache, const int64_t* cu_prefix, int64_t* prefix_len,
+                  const void* k_tree, const void* v_tree, const int32_t* acc_nodes,
+                  const int32_t* accept_len, int S, int B, int L, int Hkv, int D, int dtype,
+                  int32_t* appended, void* stream);
 
 /* ---------------------------------------------------------------- step 5
  * Greedy tree walk (運作流程 step 4): from the root, take the target's greedy

@@ -74,10 +74,10 @@ def test_draft_tree_validation():
     a = [_fake(i) for i in range(1, 20)]
 
     def call(S=1, L=4, V=64, K=4, B=8, stride=64, ws_bytes=1 << 20, logits=a[0]):
-        return f(logits, stride, a[1], a[2], S, L, V, K, B, a[3], a[4], a[5], a[6], a[7], a[8],
-                 a[9], a[10], a[11], a[12], ws_bytes, None)
+        return f(logits, stride, a[1], a[2], None, S, L, V, K, B, a[3], a[4], a[5], a[6], a[7],
+                 a[8], a[9], a[10], a[11], a[12], ws_bytes, None)
     assert call(logits=None) == -1
-    assert f(a[0], 64, a[1], a[2], 1, 4, 64, 4, 8, None, a[4], a[5], a[6], a[7], a[8], a[9],
+    assert f(a[0], 64, a[1], a[2], None, 1, 4, 64, 4, 8, None, a[4], a[5], a[6], a[7], a[8], a[9],
              a[10], a[11], a[12], 1 << 20, None) == -1   # top-K outputs are required
     assert call(S=0) == -1
     assert call(L=65) == -1
@@ -93,9 +93,9 @@ def test_draft_tree_validation():
 def test_mask_validation():
     f = ddt.load().ddt_tree_mask
     a = [_fake(i) for i in range(1, 10)]
-    assert f(a[0], a[1], a[2], None, 1, 8, None, None, None) == -1
-    assert f(a[0], a[1], a[2], None, 0, 8, a[3], None, None) == -1
-    assert f(a[0], a[1], a[2], None, 1, 1024, a[3], None, None) == -1
+    assert f(a[0], a[1], a[2], None, None, 1, 8, None, None, None) == -1
+    assert f(a[0], a[1], a[2], None, None, 0, 8, a[3], None, None) == -1
+    assert f(a[0], a[1], a[2], None, None, 1, 1024, a[3], None, None) == -1
 
 
 def test_attention_validation():
@@ -103,8 +103,8 @@ def test_attention_validation():
     a = [_fake(i) for i in range(1, 12)]
 
     def call(S=1, B=8, Hq=4, Hkv=2, D=128, dt=1, scale=0.1, maxp=64, ws_bytes=0, q=a[0]):
-        return f(q, a[1], a[2], a[3], a[4], a[5], a[6], a[7], S, B, Hq, Hkv, D, dt, scale, maxp,
-                 a[8], None, a[9], ws_bytes, None)
+        return f(q, a[1], a[2], a[3], None, a[4], a[5], a[6], a[7], S, B, Hq, Hkv, D, dt, scale,
+                 maxp, a[8], None, a[9], ws_bytes, None)
     assert call(q=None) == -1
     assert call(Hq=6, Hkv=4) == -1        # Hq % Hkv
     assert call(D=96) == -2               # no kernel for D=96
@@ -114,6 +114,21 @@ def test_attention_validation():
     assert call(scale=float("nan")) == -1
     assert call(maxp=-1) == -1
     assert call(B=1024) == -1
+
+
+def test_commit_validation():
+    f = ddt.load().ddt_commit_kv
+    a = [_fake(i) for i in range(1, 12)]
+
+    def call(S=1, B=8, L=4, Hkv=2, D=128, dt=1, kc=a[0], kt=a[4]):
+        return f(kc, a[1], a[2], a[3], kt, a[5], a[6], a[7], S, B, L, Hkv, D, dt, None, None)
+    assert call(kc=None) == -1
+    assert call(S=0) == -1
+    assert call(L=65) == -1
+    assert call(B=1024) == -1
+    assert call(D=96) == -2
+    assert call(dt=3) == -2
+    assert call(kt=ctypes.c_void_p(0x1008)) == -1     # not 16-byte aligned
 
 
 def test_walk_validation():
