@@ -284,3 +284,16 @@ def seq_tree_inputs(cfg: Config, seq: int, g: Sequence[int], tree_tok: np.ndarra
         q[n], kt[n], vt[n] = x["q"], x["k"], x["v"]
         tl[n] = seq_target_row(cfg, seq, ctx)
     return {"q": q, "k_tree": kt, "v_tree": vt, "target": tl}
+
+
+# ----------------------------------------------------------------------------- sampling noise
+_T_GUMBEL = 30
+
+
+def gumbel_noise(cfg: Config, seq: int, rnd: int = 0) -> np.ndarray:
+    """Standard Gumbel draws [L + 1, V] fp32 for one sequence's round ``rnd``: row d is
+    the noise of the target's sampling step at depth d (shared by every node of that
+    depth).  These are the random numbers the sampling rule consumes; both the oracle
+    and the library take them as an input."""
+    r = _rng(cfg.cfg_id, seq, _T_GUMBEL, rnd)
+    return r.gumbel(size=(cfg.L + 1, cfg.V)).astype(np.float32)

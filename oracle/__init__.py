@@ -5,8 +5,8 @@ CPU-baseline leg, never by the library's product path.
 """
 from .ddtree import (  # noqa: F401
     ancestors, attend, best_first_prefixes, build_tree, candidate_logprobs,
-    expected_acceptance, greedy_token, position_ids, selection_gap, softmax_topk_row,
-    topk, tree_attention, tree_mask, tree_walk, visible_nodes,
+    expected_acceptance, greedy_token, position_ids, sample_token, selection_gap, softmax_topk_row,
+    topk, tree_attention, tree_mask, tree_walk, tree_walk_sample, visible_nodes,
 )
 from .round import verify_round  # noqa: F401
 from .rounds import commit_kv, greedy_decode, run_rounds  # noqa: F401

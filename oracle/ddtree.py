@@ -267,6 +267,51 @@ def tree_walk(tree_tok: np.ndarray, parent: np.ndarray, num_nodes: int,
             "bonus": np.int32(bonus)}
 
 
+# ============================================================================ step 5 at temperature > 0
+def sample_token(logits_row: np.ndarray, gumbel_row: np.ndarray, inv_temperature: float) -> int:
+    """The target's decoding rule at temperature T > 0 (中文摘要 counts temperature
+    among the evaluated settings; 運作流程 step 4 follows the target's decoding rule):
+    a draw from softmax(logits / T).  [R24] It is taken by the Gumbel-max rule: with
+    g_v independent standard Gumbel draws, argmax_v (x_v / T + g_v) is distributed as
+    softmax(x / T).  The scores are formed in fp32 as fl(fl(x_v * t) + g_v) with
+    t = 1/T given as an fp32 value (the precision the kernel decides in); equal scores
+    go to the smaller id."""
+    x = np.asarray(logits_row, dtype=np.float32)
+    g = np.asarray(gumbel_row, dtype=np.float32)
+    y = (x * np.float32(inv_temperature)).astype(np.float32) + g
+    y = y.astype(np.float32)
+    return int(np.flatnonzero(y == np.max(y))[0])
+
+
+def tree_walk_sample(tree_tok: np.ndarray, parent: np.ndarray, depth: np.ndarray, num_nodes: int,
+                     target_logits: np.ndarray, gumbel: np.ndarray, inv_temperature: float,
+                     L: int) -> Dict[str, np.ndarray]:
+    """Tree walk of 運作流程 step 4 at temperature > 0: as tree_walk, but the target's
+    token at node n is sample_token(target_logits[n], gumbel[depth[n]], t).  [R24]
+    The noise row is chosen by depth, not by node, so the walk emits exactly the
+    tokens that plain one-token-at-a-time sampling with the same noise emits."""
+    cur = 0
+    acc: List[int] = []
+    while True:
+        want = sample_token(target_logits[cur], gumbel[int(depth[cur])], inv_temperature)
+        nxt = -1
+        for c in range(num_nodes):
+            if int(parent[c]) == cur and int(tree_tok[c]) == want:
+                nxt = c
+                break
+        if nxt < 0:
+            bonus = want
+            break
+        acc.append(nxt)
+        cur = nxt
+    acc_nodes = np.full(L, -1, dtype=np.int32)
+    acc_tok = np.full(L, -1, dtype=np.int32)
+    acc_nodes[:len(acc)] = acc
+    acc_tok[:len(acc)] = [int(tree_tok[n]) for n in acc]
+    return {"accept_len": np.int32(len(acc)), "acc_nodes": acc_nodes, "acc_tok": acc_tok,
+            "bonus": np.int32(bonus)}
+
+
 # ============================================================================ helpers for tests
 def candidate_logprobs(logq: np.ndarray) -> np.ndarray:
     """Log-probability of every candidate prefix of the K-ary depth-L candidate
