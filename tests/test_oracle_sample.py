@@ -89,3 +89,48 @@ def test_sampling_walk_accepts_on_confident_paths():
                                     gen.gumbel_noise(cfg, seed), np.float32(1.0), cfg.L)
         total += int(w["accept_len"])
     assert total >= 6
+
+
+def test_noise_row_follows_depth_not_node_index():
+    """Hand-built tree: root 0 -> nodes 1 (token 5) and 2 (token 7); node 2 -> node 3
+    (token 9).  Flat target logits; noise row 0 favours 7, row 1 favours 9, row 2
+    favours 4, row 3 favours 5.  Sampling goes root -> 7 (node 2, depth 1) -> 9 (node
+    3, depth 2) -> 4, not a child: accept [2, 3], bonus 4."""
+    tree_tok = np.array([11, 5, 7, 9], dtype=np.int32)
+    parent = np.array([-1, 0, 0, 2], dtype=np.int32)
+    depth = np.array([0, 1, 1, 2], dtype=np.int32)
+    V, L = 12, 3
+    target = np.zeros((4, V), dtype=np.float32)
+    noise = np.zeros((L + 1, V), dtype=np.float32)
+    for d, t in enumerate([7, 9, 4, 5]):
+        noise[d, t] = 3.0
+    w = oracle.tree_walk_sample(tree_tok, parent, depth, 4, target, noise, 1.0, L)
+    assert int(w["accept_len"]) == 2
+    assert w["acc_nodes"].tolist() == [2, 3, -1] and w["acc_tok"].tolist() == [7, 9, -1]
+    assert int(w["bonus"]) == 4
+
+
+def test_sampling_walk_deep_acceptance_is_plain_sampling():
+    """A confident draft and a cool target: walks accept several tokens, through nodes
+    whose indices differ from their depths."""
+    cfg = configs.custom("sample-deep", cfg_id=703, L=6, V=200, K=3, B=40, chain_boost=9.0)
+    deepest = 0
+    for seed in range(5):
+        d = gen.draft(cfg, seed, 0)
+        keep = np.ones(cfg.L + 1, dtype=bool)   # the target follows the planted chain
+        tok, lq = oracle.topk(d["logits"], cfg.K)
+        tree = oracle.build_tree(tok, lq, d["bonus"], cfg.B)
+        nn = int(tree["num_nodes"])
+        tl = gen.target_logits(cfg, seed, 0, tree["tree_tok"], tree["parent"], nn, d["chain"], keep)
+        noise = gen.gumbel_noise(cfg, seed)
+        t = np.float32(1.0 / 0.3)
+        w = oracle.tree_walk_sample(tree["tree_tok"], tree["parent"], tree["depth"], nn, tl, noise, t, cfg.L)
+        a = int(w["accept_len"])
+        plain, path = [], ()
+        for k in range(a + 1):
+            y = oracle.sample_token(gen.target_row(cfg, seed, 0, path, d["chain"], keep), noise[k], t)
+            plain.append(y)
+            path = path + (y,)
+        assert [int(v) for v in w["acc_tok"][:a]] + [int(w["bonus"])] == plain
+        deepest = max(deepest, a)
+    assert deepest >= 3
