@@ -52,6 +52,8 @@ def load() -> ctypes.CDLL:
         "ddt_commit_kv": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]),
         "ddt_tree_walk_workspace_size": (sz, [i32, i32, i64]),
         "ddt_tree_walk": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]),
+        "ddt_tree_walk_sample": (i32, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i64, vp, vp, vp, vp,
+                                       vp, sz, vp]),
         "ddt_tree_walk_noalloc_max_bytes": (sz, []),
         "ddt_tree_walk_noalloc": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp]),
         "ddt_attention_profiling": (i32, [i32]),
@@ -69,7 +71,8 @@ def load() -> ctypes.CDLL:
 EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_build_tree",
            "ddt_tree_mask", "ddt_draft_tree_workspace_size", "ddt_draft_tree",
            "ddt_tree_attention_workspace_size", "ddt_tree_attention", "ddt_commit_kv",
-           "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_tree_walk_noalloc_max_bytes",
+           "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_tree_walk_sample",
+           "ddt_tree_walk_noalloc_max_bytes",
            "ddt_tree_walk_noalloc", "ddt_attention_profiling", "ddt_attention_timing")
 
 
@@ -304,6 +307,38 @@ def ddt_tree_walk(tree_tok, parent, num_nodes, target_logits, L: int, out=None, 
     _check(lib.ddt_tree_walk(_p(tree_tok), _p(parent), _p(num_nodes), _p(target_logits), S, N - 1,
                              L, V, _p(out["accept_len"]), _p(out["acc_nodes"]), _p(out["acc_tok"]),
                              _p(out["bonus"]), _p(ws), ws.numel(), _stream(dev)), "ddt_tree_walk")
+    return out
+
+
+def ddt_tree_walk_sample(tree_tok, parent, depth, num_nodes, target_logits, gumbel,
+                         inv_temperature: float, L: int, out=None, ws=None):
+    """Walk at temperature 1 / inv_temperature by the Gumbel-max rule; gumbel [S, L+1, V]
+    fp32 noise, row d for depth d -> dict(accept_len, acc_nodes, acc_tok, bonus)."""
+    lib = load()
+    S, N = tree_tok.shape
+    _dev(tree_tok, "tree_tok", torch.int32)
+    _dev(parent, "parent", torch.int32, (S, N))
+    _dev(depth, "depth", torch.int32, (S, N))
+    _dev(num_nodes, "num_nodes", torch.int32, (S,))
+    _dev(target_logits, "target_logits", torch.float32)
+    if target_logits.shape[:2] != (S, N):
+        raise ValueError("target_logits must be [S, N, V]")
+    V = target_logits.shape[2]
+    _dev(gumbel, "gumbel", torch.float32, (S, L + 1, V))
+    dev = tree_tok.device
+    if out is None:
+        out = {"accept_len": torch.empty(S, dtype=torch.int32, device=dev),
+               "acc_nodes": torch.empty(S, L, dtype=torch.int32, device=dev),
+               "acc_tok": torch.empty(S, L, dtype=torch.int32, device=dev),
+               "bonus": torch.empty(S, dtype=torch.int32, device=dev)}
+    need = lib.ddt_tree_walk_workspace_size(S, N - 1, V)
+    if ws is None:
+        ws = _ws(need, dev)
+    _check(lib.ddt_tree_walk_sample(_p(tree_tok), _p(parent), _p(depth), _p(num_nodes),
+                                    _p(target_logits), _p(gumbel), float(inv_temperature), S, N - 1,
+                                    L, V, _p(out["accept_len"]), _p(out["acc_nodes"]),
+                                    _p(out["acc_tok"]), _p(out["bonus"]), _p(ws), ws.numel(),
+                                    _stream(dev)), "ddt_tree_walk_sample")
     return out
 
 

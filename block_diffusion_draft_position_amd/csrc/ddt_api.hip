@@ -245,6 +245,24 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                                      as_stream(stream)));
 }
 
+int ddt_tree_walk_sample(const int32_t* tree_tok, const int32_t* parent, const int32_t* depth,
+                         const int32_t* num_nodes, const float* target_logits, const float* gumbel,
+                         float inv_temperature, int S, int B, int L, int64_t vocab,
+                         int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok,
+                         int32_t* bonus_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!tree_tok || !parent || !depth || !num_nodes || !target_logits || !gumbel || !accept_len ||
+      !acc_nodes || !acc_tok || !bonus_out)
+    return DDT_ERR_INVALID_ARG;
+  if (S < 1 || L < 1 || L > DDT_MAX_L || B < 0 || B > DDT_MAX_B || vocab < 1 || vocab > INT32_MAX)
+    return DDT_ERR_INVALID_ARG;
+  if (!(inv_temperature >= 0.f) || !isfinite(inv_temperature)) return DDT_ERR_INVALID_ARG;
+  const WalkPlan plan = walk_plan(S, B, vocab);
+  if (!ws || ws_bytes < plan.ws_bytes) return DDT_ERR_WORKSPACE;
+  return hip_status(launch_tree_walk(tree_tok, parent, num_nodes, target_logits, S, B, L, vocab,
+                                     accept_len, acc_nodes, acc_tok, bonus_out, ws, plan,
+                                     as_stream(stream), depth, gumbel, inv_temperature));
+}
+
 int ddt_tree_walk_noalloc(const int32_t* tree_tok, const int32_t* parent, const int32_t* num_nodes,
                           const float* target_logits, int S, int B, int L, int64_t vocab,
                           int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok,

@@ -207,7 +207,7 @@ hipError_t launch_tree_attention(const void* q, const void* kc, const void* vc,
                                  int Hq, int Hkv, int D, float scale, void* out, float* lse,
                                  void* ws, const AttnPlan& plan, hipStream_t st);
 
-// walk
+// walk (greedy, or with gumbel [S, L+1, vocab] and depth: sampling at 1 / inv_t)
 struct WalkPlan {
   int waves;             // waves per workgroup
   int nbatch;            // batches of waves * 64 * 32 logits per row: one workgroup each
@@ -226,7 +226,8 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             const int32_t* num_nodes, const float* target, int S, int B, int L,
                             int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,
                             int32_t* acc_tok, int32_t* bonus_out, void* ws, const WalkPlan& plan,
-                            hipStream_t st);
+                            hipStream_t st, const int32_t* depth = nullptr,
+                            const float* gumbel = nullptr, float inv_t = 1.f);
 
 // KV commit: appends each sequence's root and accepted nodes' tree K/V rows to its
 // cache region and advances prefix_len (one workgroup per sequence).

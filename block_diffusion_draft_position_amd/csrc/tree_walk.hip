@@ -57,15 +57,28 @@ __device__ __forceinline__ int unpack_id(unsigned long long key) {
   return (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
 }
 
+// The sampling score fl(fl(x * t) + g): contraction into a fused multiply-add would
+// round once instead of twice and could change the arg-max, so it is switched off here.
+__device__ __forceinline__ float sample_score(float x, float t, float g) {
+#pragma clang fp contract(off)
+  return x * t + g;
+}
+
 // ONE: the whole grid runs at once, so the scan is on the latency path and takes the
 // batch maximum first (a short dependent chain); when workgroups stream in rounds, the
 // compare-as-you-go scan keeps up with the loads better (measured).  Two workgroups
 // per CU (8 waves per SIMD, at most 64 VGPRs): the row loads of one hide the other's scan.
-template <bool ONE>
-__global__ void __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
+// SAMPLE: temperature sampling by the Gumbel-max rule.  The score of token v at node n
+// is fl(fl(x_v * inv_t) + g[s, depth(n), v]), an fp32 multiply and an fp32 add each
+// rounded on its own (sample_score), so the arg-max is decided in the same arithmetic
+// as the definition; the noise row is shared by a depth's nodes and read through the
+// caches.  It holds two rows' loads at once, so it runs four waves per SIMD.
+template <bool ONE, bool SAMPLE>
+__global__ void __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 4 : 8, 8)))
 tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ parent,
-                 const int32_t* __restrict__ num_nodes, const float* __restrict__ target, int N,
-                 int L, int vocab, int nseg, bool vec_ok, unsigned long long* __restrict__ best,
+                 const int32_t* __restrict__ num_nodes, const float* __restrict__ target,
+                 const int32_t* __restrict__ depth, const float* __restrict__ gumbel, float inv_t,
+                 int N, int L, int vocab, int nseg, bool vec_ok, unsigned long long* __restrict__ best,
                  unsigned* __restrict__ counters, unsigned* __restrict__ rowcnt,
                  int32_t* __restrict__ accept_len,
                  int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
@@ -83,6 +96,8 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const float* x = target + row * (int64_t)vocab;
+  const float* gn = nullptr;
+  if constexpr (SAMPLE) gn = gumbel + ((int64_t)s * (L + 1) + depth[row]) * vocab;
 
   float bv = -INFINITY;
   int bi = INT_MAX;
@@ -94,11 +109,24 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
       const int base = lo + (b * kWave + lane) * 4;
       if (vec_ok && base + 3 < vocab) {
         const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + base));
+        if constexpr (SAMPLE) {
+          const f32x4 g = *reinterpret_cast<const f32x4*>(gn + base);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[4 * b + q] = t[q];
+          for (int q = 0; q < 4; ++q) v[4 * b + q] = sample_score(t[q], inv_t, g[q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[4 * b + q] = t[q];
+        }
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[4 * b + q] = base + q < vocab ? x[base + q] : -INFINITY;
+        for (int q = 0; q < 4; ++q) {
+          float e = -INFINITY;
+          if (base + q < vocab) {
+            e = x[base + q];
+            if constexpr (SAMPLE) e = sample_score(e, inv_t, gn[base + q]);
+          }
+          v[4 * b + q] = e;
+        }
       }
     }
     if constexpr (ONE) {
@@ -283,23 +311,32 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             const int32_t* num_nodes, const float* target, int S, int B, int L,
                             int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,
                             int32_t* acc_tok, int32_t* bonus_out, void* ws, const WalkPlan& plan,
-                            hipStream_t st) {
+                            hipStream_t st, const int32_t* depth, const float* gumbel,
+                            float inv_t) {
   const int N = B + 1;
   unsigned* counters = static_cast<unsigned*>(ws);
   unsigned* rowcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + plan.counter_bytes);
   unsigned long long* best = reinterpret_cast<unsigned long long*>(
       static_cast<char*>(ws) + plan.counter_bytes + plan.rowcnt_bytes);
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0);
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0) &&
+                      (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0);
   const dim3 grid((unsigned)((int64_t)S * N * plan.nbatch)), block(plan.waves * kWave);
   const size_t smem = 3 * sizeof(int) * N;
-  if (plan.short_scan)
-    hipLaunchKernelGGL(tree_walk_kernel<true>, grid, block, smem, st, tree_tok, parent, num_nodes,
-                       target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, rowcnt,
-                       accept_len, acc_nodes, acc_tok, bonus_out);
-  else
-    hipLaunchKernelGGL(tree_walk_kernel<false>, grid, block, smem, st, tree_tok, parent, num_nodes,
-                       target, N, L, (int)vocab, plan.nbatch, vec_ok, best, counters, rowcnt,
-                       accept_len, acc_nodes, acc_tok, bonus_out);
+#define DDT_WALK(ONE, SAMPLE)                                                                  \
+  hipLaunchKernelGGL((tree_walk_kernel<ONE, SAMPLE>), grid, block, smem, st, tree_tok, parent, \
+                     num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, plan.nbatch,     \
+                     vec_ok, best, counters, rowcnt, accept_len, acc_nodes, acc_tok, bonus_out)
+  if (gumbel) {
+    if (plan.short_scan)
+      DDT_WALK(true, true);
+    else
+      DDT_WALK(false, true);
+  } else if (plan.short_scan) {
+    DDT_WALK(true, false);
+  } else {
+    DDT_WALK(false, false);
+  }
+#undef DDT_WALK
   return hipGetLastError();
 }
 

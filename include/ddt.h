@@ -272,6 +272,31 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                   int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok, int32_t* bonus_out,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- step 5 at temperature > 0
+ * Tree walk under the target's sampling rule at temperature T > 0 (中文摘要 counts
+ * temperature among the evaluated settings; 運作流程 step 4 follows the target's
+ * decoding rule): the target's token at node n is a draw from softmax(logits / T),
+ * taken by the Gumbel-max rule,
+ *   token(n) = argmax_v  fl( fl(target_logits[s, n, v] * inv_temperature)
+ *                            + gumbel[s, depth[s, n], v] ),
+ * each fp32 multiply and add rounded on its own (no fused multiply-add), equal scores
+ * to the smaller token id (-0 and +0 equal).  The walk then proceeds as ddt_tree_walk.
+ * The noise row is chosen by the node's depth, so every node of a depth shares it and
+ * the walk emits exactly the tokens that plain one-token-at-a-time sampling with the
+ * same noise emits (lossless).
+ *
+ * depth            [S, N] from ddt_build_tree.
+ * gumbel           [S, L + 1, vocab] fp32 standard Gumbel draws, the caller's random
+ *                  numbers for this round (row d serves depth d); finite.
+ * inv_temperature  1 / T as an fp32 value, finite and >= 0 (0 samples uniformly).
+ * Other arguments, outputs, workspace (the same size) and errors as ddt_tree_walk.
+ */
+int ddt_tree_walk_sample(const int32_t* tree_tok, const int32_t* parent, const int32_t* depth,
+                         const int32_t* num_nodes, const float* target_logits, const float* gumbel,
+                         float inv_temperature, int S, int B, int L, int64_t vocab,
+                         int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok,
+                         int32_t* bonus_out, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- step 5, no allocation
  * ddt_tree_walk without a workspace argument, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid

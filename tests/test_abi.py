@@ -145,6 +145,22 @@ def test_walk_validation():
     assert call(ws_bytes=lib.ddt_tree_walk_workspace_size(1, 8, 64) - 1) == -3
 
 
+def test_walk_sample_validation():
+    lib = ddt.load()
+    f = lib.ddt_tree_walk_sample
+    a = [_fake(i) for i in range(1, 14)]
+
+    def call(S=1, B=8, L=4, V=64, t=1.0, ws_bytes=1 << 20, g=a[5]):
+        return f(a[0], a[1], a[2], a[3], a[4], g, t, S, B, L, V, a[6], a[7], a[8], a[9], a[10],
+                 ws_bytes, None)
+    assert call(g=None) == -1
+    assert call(t=-1.0) == -1
+    assert call(t=float("inf")) == -1
+    assert call(t=float("nan")) == -1
+    assert call(L=65) == -1
+    assert call(ws_bytes=lib.ddt_tree_walk_workspace_size(1, 8, 64) - 1) == -3
+
+
 def test_walk_noalloc_validation():
     """The allocation-free walk rejects a problem whose workspace exceeds its static
     scratch (1 MiB) before any launch, and validates like ddt_tree_walk."""
