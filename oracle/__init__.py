@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the bench's
 CPU-baseline leg, never by the library's product path.
 """
 from .ddtree import (  # noqa: F401
-    ancestors, attend, best_first_prefixes, build_tree, candidate_logprobs,
-    expected_acceptance, greedy_token, position_ids, sample_token, selection_gap, softmax_topk_row,
+    ancestors, attend, best_first_prefixes, build_tree, candidate_logprobs, choose_budget,
+    expected_acceptance, greedy_token, position_ids, prune_tree, sample_token, score_order,
+    selection_gap, softmax_topk_row,
     topk, tree_attention, tree_mask, tree_walk, tree_walk_sample, visible_nodes,
 )
 from .round import verify_round  # noqa: F401

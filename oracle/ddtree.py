@@ -312,6 +312,52 @@ def tree_walk_sample(tree_tok: np.ndarray, parent: np.ndarray, depth: np.ndarray
             "bonus": np.int32(bonus)}
 
 
+# ============================================================================ adaptive budget
+def score_order(node_logq: np.ndarray, num_nodes: int) -> List[int]:
+    """The tree's non-root nodes in the heap's pop order: log-probability descending,
+    equal values by canonical index (shallower first, then lexicographic rank path,
+    which is the canonical order within a depth [R5])."""
+    return sorted(range(1, num_nodes), key=lambda n: (-float(node_logq[n]), n))
+
+
+def choose_budget(node_logq: np.ndarray, num_nodes: int, cost: np.ndarray) -> Tuple[int, float]:
+    """[R25] The budget B* <= num_nodes - 1 that maximises tokens per unit of verify
+    cost, (E[accept](b) + 1) / cost[b] (實驗結果與權衡: speedup peaks at an
+    intermediate budget; 理論基礎 Prop. 1: E[accept](b) is the sum of the b largest
+    prefix probabilities, the first b pops of the heap).  cost[b] > 0 is the caller's
+    verify cost at budget b.  Sums and ratios in fp64; equal ratios to the smaller b.
+    Returns (B*, E[accept](B*))."""
+    order = score_order(node_logq, num_nodes)
+    e = 0.0
+    best_b, best_j, best_e = 0, (0.0 + 1.0) / float(cost[0]), 0.0
+    for b in range(1, num_nodes):
+        e += float(np.exp(float(node_logq[order[b - 1]])))
+        j = (e + 1.0) / float(cost[b])
+        if j > best_j:
+            best_b, best_j, best_e = b, j, e
+    return best_b, best_e
+
+
+def prune_tree(tree: Dict[str, np.ndarray], b: int) -> Dict[str, np.ndarray]:
+    """The tree cut to its b most probable prefixes (the first b pops): they are
+    prefix-closed (Prop. 2), and keeping the survivors in their canonical order keeps
+    the order canonical [R5].  Arrays keep their length; the rest is padding."""
+    nn = int(tree["num_nodes"])
+    keep = [0] + sorted(score_order(tree["node_logq"], nn)[:b])
+    new = {old: i for i, old in enumerate(keep)}
+    N = tree["tree_tok"].shape[0]
+    out = {"tree_tok": np.full(N, -1, dtype=np.int32), "parent": np.full(N, -1, dtype=np.int32),
+           "depth": np.full(N, -1, dtype=np.int32), "node_logq": np.full(N, -np.inf, dtype=np.float64)}
+    for i, old in enumerate(keep):
+        out["tree_tok"][i] = tree["tree_tok"][old]
+        out["depth"][i] = tree["depth"][old]
+        out["node_logq"][i] = tree["node_logq"][old]
+        p = int(tree["parent"][old])
+        out["parent"][i] = -1 if p < 0 else new[p]
+    out["num_nodes"] = np.int32(len(keep))
+    return out
+
+
 # ============================================================================ helpers for tests
 def candidate_logprobs(logq: np.ndarray) -> np.ndarray:
     """Log-probability of every candidate prefix of the K-ary depth-L candidate
