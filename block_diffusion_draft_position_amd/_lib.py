@@ -49,6 +49,7 @@ def load() -> ctypes.CDLL:
         "ddt_tree_attention_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i64]),
         "ddt_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                      i32, f32, i64, vp, vp, vp, sz, vp]),
+        "ddt_adapt_budget": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "ddt_commit_kv": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]),
         "ddt_tree_walk_workspace_size": (sz, [i32, i32, i64]),
         "ddt_tree_walk": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]),
@@ -70,7 +71,8 @@ def load() -> ctypes.CDLL:
 
 EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_build_tree",
            "ddt_tree_mask", "ddt_draft_tree_workspace_size", "ddt_draft_tree",
-           "ddt_tree_attention_workspace_size", "ddt_tree_attention", "ddt_commit_kv",
+           "ddt_adapt_budget", "ddt_tree_attention_workspace_size", "ddt_tree_attention",
+           "ddt_commit_kv",
            "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_tree_walk_sample",
            "ddt_tree_walk_noalloc_max_bytes",
            "ddt_tree_walk_noalloc", "ddt_attention_profiling", "ddt_attention_timing")
@@ -208,6 +210,26 @@ def ddt_draft_tree(logits: torch.Tensor, bonus: torch.Tensor, cu_prefix: Optiona
                               _p(out.get("pos_ids")), _p(ws), ws.numel(), _stream(dev)),
            "ddt_draft_tree")
     return out
+
+
+def ddt_adapt_budget(tree: Dict[str, torch.Tensor], cost: torch.Tensor):
+    """Cut each sequence's tree (a ddt_build_tree dict, modified in place) to the budget
+    that maximises (E[accept] + 1) / cost[b]; cost [B+1] fp32 on the device.
+    Returns (budget [S] int32, expected acceptance [S] fp32)."""
+    lib = load()
+    S, N = tree["tree_tok"].shape
+    for k in ("tree_tok", "parent", "depth"):
+        _dev(tree[k], k, torch.int32, (S, N))
+    _dev(tree["node_logq"], "node_logq", torch.float32, (S, N))
+    _dev(tree["num_nodes"], "num_nodes", torch.int32, (S,))
+    _dev(cost, "cost", torch.float32, (N,))
+    dev = cost.device
+    budget = torch.empty(S, dtype=torch.int32, device=dev)
+    expected = torch.empty(S, dtype=torch.float32, device=dev)
+    _check(lib.ddt_adapt_budget(_p(cost), S, N - 1, _p(tree["tree_tok"]), _p(tree["parent"]),
+                                _p(tree["depth"]), _p(tree["node_logq"]), _p(tree["num_nodes"]),
+                                _p(budget), _p(expected), _stream(dev)), "ddt_adapt_budget")
+    return budget, expected
 
 
 def attention_workspace_size(S, B, Hq, Hkv, D, dtype, max_prefix) -> int:

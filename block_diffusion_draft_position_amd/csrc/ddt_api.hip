@@ -203,6 +203,17 @@ int ddt_tree_attention(const void* q, const void* k_cache, const void* v_cache,
                                           as_stream(stream)));
 }
 
+// ------------------------------------------------------------------ adaptive budget
+int ddt_adapt_budget(const float* cost, int S, int B, int32_t* tree_tok, int32_t* parent,
+                     int32_t* depth, float* node_logq, int32_t* num_nodes, int32_t* budget_out,
+                     float* expected_out, void* stream) {
+  if (!cost || !tree_tok || !parent || !depth || !node_logq || !num_nodes || !budget_out)
+    return DDT_ERR_INVALID_ARG;
+  if (S < 1 || B < 0 || B > DDT_MAX_B) return DDT_ERR_INVALID_ARG;
+  return hip_status(launch_adapt_budget(cost, S, B, tree_tok, parent, depth, node_logq, num_nodes,
+                                        budget_out, expected_out, as_stream(stream)));
+}
+
 // ------------------------------------------------------------------ KV commit
 int ddt_commit_kv(void* k_cache, void* v_cache, const int64_t* cu_prefix, int64_t* prefix_len,
                   const void* k_tree, const void* v_tree, const int32_t* acc_nodes,

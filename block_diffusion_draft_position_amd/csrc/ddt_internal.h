@@ -229,6 +229,12 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             hipStream_t st, const int32_t* depth = nullptr,
                             const float* gumbel = nullptr, float inv_t = 1.f);
 
+// adaptive budget: per sequence, B* from the tree's scores and the cost table, and the
+// tree cut to its top-B* prefixes in place (one workgroup per sequence)
+hipError_t launch_adapt_budget(const float* cost, int S, int B, int32_t* tree_tok, int32_t* parent,
+                               int32_t* depth, float* node_logq, int32_t* num_nodes,
+                               int32_t* budget_out, float* expected_out, hipStream_t st);
+
 // KV commit: appends each sequence's root and accepted nodes' tree K/V rows to its
 // cache region and advances prefix_len (one workgroup per sequence).
 hipError_t launch_commit_kv(void* k_cache, void* v_cache, const int64_t* cu_prefix,

@@ -182,6 +182,32 @@ int ddt_draft_tree(const float* logits, int64_t row_stride, const int32_t* bonus
                    int32_t* depth, float* node_logq, int32_t* num_nodes, uint32_t* mask,
                    int32_t* pos_ids, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- adaptive budget (after step 2)
+ * Choice of the node budget per sequence (實驗結果與權衡: the speedup peaks at an
+ * intermediate budget as verification cost grows; 理論基礎: by Proposition 1 the
+ * expected acceptance E(b) of the best tree with b nodes is the sum of its prefix
+ * probabilities, and by Proposition 2 that tree is the b most probable prefixes, the
+ * heap's first b pops).  For a tree built at budget B:
+ *   B*_s = argmax over b = 0 .. num_nodes[s]-1 of (E(b) + 1) / cost[b]
+ * (sums and ratios in fp64; equal ratios to the smaller b), and the tree is cut, in
+ * place, to its B*_s most probable prefixes: pop order is log-probability
+ * descending, equal values by smaller node index (shallower first, then canonical
+ * order within a depth).  The survivors keep their canonical order and are
+ * renumbered; entries past B*_s + 1 become padding.  Call ddt_tree_mask afterwards
+ * for the cut tree's mask; attention and walk honour the new num_nodes.
+ *
+ * cost        [B+1] fp32 device array: the caller's verify cost at each budget
+ *             (for instance measured microseconds per round); finite and > 0.
+ * tree_tok, parent, depth, node_logq, num_nodes: as written by ddt_build_tree
+ *             (node_logq required), rewritten in place.
+ * budget_out  [S] int32: B*_s.
+ * expected_out nullable [S] fp32: E(B*_s).
+ * Errors: null required pointer; S < 1; B outside [0, DDT_MAX_B].
+ */
+int ddt_adapt_budget(const float* cost, int S, int B, int32_t* tree_tok, int32_t* parent,
+                     int32_t* depth, float* node_logq, int32_t* num_nodes, int32_t* budget_out,
+                     float* expected_out, void* stream);
+
 /* ---------------------------------------------------------------- step 4 (attention)
  * Grouped-query tree attention: the whole tree is scored in one target forward
  * under the ancestor-only mask (運作流程 step 3).

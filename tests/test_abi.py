@@ -116,6 +116,15 @@ def test_attention_validation():
     assert call(B=1024) == -1
 
 
+def test_adapt_budget_validation():
+    f = ddt.load().ddt_adapt_budget
+    a = [_fake(i) for i in range(1, 12)]
+    assert f(None, 1, 8, a[1], a[2], a[3], a[4], a[5], a[6], None, None) == -1
+    assert f(a[0], 1, 8, a[1], a[2], a[3], None, a[5], a[6], None, None) == -1   # scores required
+    assert f(a[0], 0, 8, a[1], a[2], a[3], a[4], a[5], a[6], None, None) == -1
+    assert f(a[0], 1, 1024, a[1], a[2], a[3], a[4], a[5], a[6], None, None) == -1
+
+
 def test_commit_validation():
     f = ddt.load().ddt_commit_kv
     a = [_fake(i) for i in range(1, 12)]
