@@ -193,6 +193,8 @@ int ddt_tree_attention(const void* q, const void* k_cache, const void* v_cache,
   const int c = attn_check(S, B, Hq, Hkv, D, dtype);
   if (c != DDT_OK) return c;
   if (!(scale > 0.f) || !isfinite(scale) || max_prefix < 0) return DDT_ERR_INVALID_ARG;
+  // the bf16 kernels address a tile's 64 key rows with 32-bit byte offsets
+  if (dtype == DDT_BF16 && (int64_t)Hkv * D * 2 * 64 > INT32_MAX) return DDT_ERR_UNSUPPORTED;
   const AttnPlan plan = attn_plan(S, B, Hq, Hkv, D, dtype, max_prefix);
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return DDT_ERR_WORKSPACE;
   if ((int64_t)S * Hkv * (plan.nsplit + 1) * plan.row_groups + 8 * (int64_t)plan.row_groups > INT32_MAX)

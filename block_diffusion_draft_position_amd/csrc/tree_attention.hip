@@ -325,7 +325,7 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 
 // ---------------------------------------------------------------- bf16, D = 128 (gfx950 path)
 // Same decomposition as attn_partial_bf16, rebuilt around gfx950 features:
-//   * K and V tiles (64 keys) go global -> LDS with global_load_lds_dwordx4, no
+//   * K and V tiles (64 keys) go global -> LDS with buffer_load_dwordx4 ... lds, no
 //     registers in between, into a 2-stage ring: tile t + 1 is issued right after
 //     the barrier that opens tile t, so one tile is in flight while one is consumed.
 //     One barrier per tile suffices: the stage refilled after barrier t was last
@@ -336,13 +336,21 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 //   * V stays row-major; the PV operand V^T is read with ds_read_b64_tr_b16, which
 //     hands each lane of a 16-lane group one head-dim column of a 4-key block.
 //   * v_mfma_f32_16x16x32_bf16 with 32 query rows per wave (two 16-row blocks that
-//     share every K/V fragment read from LDS).
+//     share every K/V fragment read from LDS).  QK^T runs head-dim step outermost, so
+//     eight independent accumulators alternate, and the next step's K fragments are read
+//     while a step's MFMAs run; PV goes through head-dim blocks in pairs, the next
+//     pair's V fragments read while a pair's MFMAs run (a wave waits on LDS three or
+//     four times per product instead of eight).
+//   * The per-sequence bounds, the split's length and the tile index live in scalar
+//     registers, a full tile's loads need one lane offset in all, and the rare paths (a
+//     split's partial last tile, the lazy rescale) are real branches: left to itself
+//     the compiler turned them into selects executed on every tile.  The kernel fits
+//     in 256 registers without spilling at every workgroup width.
 //   * The running max is raised only when a tile's max exceeds it by more than
 //     2^8; otherwise O and l are not rescaled (p <= 2^8 stays exact in fp32/bf16).
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void glob_void;
 
 constexpr int kStages = 2;
 constexpr int kTileBytes = kTile * 128 * 2;      // one K or V tile, D = 128
@@ -375,6 +383,14 @@ __device__ __forceinline__ unsigned char* ring_v() {
 // transposed V read get slot offsets that differ in bits 1-3 with bit 0 equal, so
 // with the two chunks (c, c ^ 1) they fill sixteen different slots per 32 lanes.
 // (Measured: a variant aimed at 32 banks doubled the bank-conflict cycles.)
+__device__ __forceinline__ int64_t rfl64(int64_t v) {
+  const int lo32 = __builtin_amdgcn_readfirstlane((int)(v & 0xffffffff));
+  const int hi32 = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi32 << 32) | (uint32_t)lo32);
+}
+
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer: 32-bit data format
+
 __device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
 
 template <int NW>
@@ -400,9 +416,11 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   // remainder) issues its share of the tile loads and meets the barriers, no more
   const bool live = (u.rg * NW + wave) * 32 < R;
 
-  const int nn = num_nodes[u.s];
-  const int64_t p0 = pre.start(u.s);
-  const int64_t P = kc ? pre.length(u.s) : 0;
+  // per-sequence bounds, uniform across the workgroup: kept in scalar registers so that
+  // the tile loop's bounds, tail tests and branches are scalar
+  const int nn = __builtin_amdgcn_readfirstlane(num_nodes[u.s]);
+  const int64_t p0 = rfl64(pre.start(u.s));
+  const int64_t P = kc ? rfl64(pre.length(u.s)) : 0;
   const int64_t kstride = (int64_t)Hkv * D;
   const bool tree = u.c == nsplit;
   int64_t lo, hi;
@@ -413,42 +431,69 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     if (u.c >= nvalid) return;
     lo = (int64_t)u.c * chunk;
     hi = (u.c == nvalid - 1) ? P : lo + chunk;
-    kb = kc + (p0 * Hkv + u.g) * D;
-    vb = vc + (p0 * Hkv + u.g) * D;
+    kb = kc + ((p0 + lo) * Hkv + u.g) * D;
+    vb = vc + ((p0 + lo) * Hkv + u.g) * D;
   } else {
     lo = 0;
     hi = nn;
     kb = kt + ((int64_t)u.s * N * Hkv + u.g) * D;
     vb = vt + ((int64_t)u.s * N * Hkv + u.g) * D;
   }
-  const int ntiles = (int)((hi - lo + kTile - 1) / kTile);
+  // the split's key count and tiles, uniform (readfirstlane: else the compiler keeps
+  // them in vector registers and every per-tile test becomes a divergent branch)
+  const int64_t span = rfl64(hi - lo);
+  const int ntiles = __builtin_amdgcn_readfirstlane((int)((span + kTile - 1) / kTile));
 
   // ---- the loads of tile t into ring stage ST: 32 instructions of 1 KB (4 key rows),
   // 16 for K then 16 for V, dealt round robin to the waves.  Rows past the split
-  // (last tile) re-read the split's last row and are masked later.  A lane's element
-  // offset within a full tile is fixed, so it is formed once; per tile only the
-  // (uniform) tile base changes.
-  int loff[NLOAD];
+  // (last tile) re-read the split's last row and are masked later.
+  // Tile loads go through buffer resources based at the tile's first row (one for K, one
+  // for V; rebuilt per tile with scalar arithmetic): a scalar byte offset carries the
+  // load's row block, a 32-bit lane offset the rest, so no 64-bit address is formed per
+  // lane and offsets stay below 64 rows whatever the split's length.  A load's key row
+  // is 4 * (i & 15) + g4 and its swizzle splits into disjoint bits, 2 g4 from the lane
+  // and 8 (i & 1) + (i >> 1 & 1) from the (uniform) load index; a row is 256-byte
+  // aligned, so the lane offset of a full tile's load is one lane base XOR a uniform
+  // constant.  (The bases pass through readfirstlane: the compiler then knows them to
+  // be uniform, else it wraps every load in a loop over the wave's distinct resources.)
+  const unsigned char* kbu = (const unsigned char*)rfl64((int64_t)kb);
+  const unsigned char* vbu = (const unsigned char*)rfl64((int64_t)vb);
+  const uint32_t rowb = (uint32_t)kstride * 2;  // bytes per key row, a multiple of 256
+  const uint32_t lane_base = (uint32_t)g4 * rowb + (uint32_t)((l16 ^ (2 * g4)) * 16);
+  auto issue = [&]<int ST>(int t_) {
+    const int t = __builtin_amdgcn_readfirstlane(t_);
+    const int64_t t0 = (int64_t)t * kTile;  // from lo
+    const int64_t tb = t0 * rowb;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbu + tb), (short)0, -1, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbu + tb), (short)0, -1, kRsrcWord3);
+    if (t0 + kTile <= span) {
 #pragma unroll
-  for (int j = 0; j < NLOAD; ++j) {
-    const int key = 4 * (((wave + j * NW) & 31) & 15) + g4;
-    loff[j] = key * (int)kstride + (l16 ^ swz(key)) * 8;
-  }
-  auto issue = [&]<int ST>(int t) {
-    const int64_t t0 = lo + (int64_t)t * kTile;
-    const bool full = t0 + kTile <= hi;
-#pragma unroll
-    for (int j = 0; j < NLOAD; ++j) {
-      const int i = (wave + j * NW) & 31;
-      const bool isv = i >= 16;
-      const bf16_t* base = (isv ? vb : kb) + t0 * kstride;
-      int off = loff[j];
-      if (!full) {
-        const int key = min(4 * (i & 15) + g4, (int)(hi - 1 - t0));
-        off = key * (int)kstride + (l16 ^ swz(4 * (i & 15) + g4)) * 8;
+      for (int j = 0; j < NLOAD; ++j) {
+        const int i = (wave + j * NW) & 31;
+        const bool isv = i >= 16;
+        unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + (i & 15) * 1024;
+        const uint32_t x = 16u * (8u * (i & 1) + ((i >> 1) & 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_void*)dst, 16, lane_base ^ x,
+                                                 (uint32_t)(4 * (i & 15)) * rowb, 0, 0);
       }
-      unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + (i & 15) * 1024;
-      __builtin_amdgcn_global_load_lds((glob_void*)(base + off), (lds_void*)dst, 16, 0, 0);
+    } else {
+      // the split's last, partial tile: rows past the split re-read its last row.  (The
+      // lane terms pass through an empty asm so that the per-load offsets are formed
+      // here, not hoisted out of the tile loop and kept live.)
+      asm volatile("" ::: "memory");
+      int gl = g4;
+      uint32_t lchunk = (uint32_t)((l16 ^ (2 * g4)) * 16);
+      asm volatile("" : "+v"(gl), "+v"(lchunk));
+      const int last = (int)(span - 1 - t0);
+#pragma unroll
+      for (int j = 0; j < NLOAD; ++j) {
+        const int i = (wave + j * NW) & 31;
+        const bool isv = i >= 16;
+        const int key = min(4 * (i & 15) + gl, last);
+        const uint32_t off = (uint32_t)key * rowb + (lchunk ^ (16u * (8u * (i & 1) + ((i >> 1) & 1))));
+        unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + (i & 15) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_void*)dst, 16, off, 0, 0, 0);
+      }
     }
   };
 
@@ -467,8 +512,11 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     for (int kk = 0; kk < 4; ++kk)
       qf[qb][kk] = okq[qb] ? *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + g4 * 8) : bf16x8{};
   }
-  const uint32_t* mrow0 = mask + ((int64_t)u.s * N + (okq[0] ? nodeq[0] : 0)) * W;
-  const uint32_t* mrow1 = mask + ((int64_t)u.s * N + (okq[1] ? nodeq[1] : 0)) * W;
+  // the sequence's mask (uniform base) and this lane's two rows in it, as 32-bit byte
+  // offsets: the word loads take the scalar-base form
+  const unsigned char* mseq = (const unsigned char*)(mask + (int64_t)u.s * N * W);
+  const uint32_t mrow0 = (uint32_t)((okq[0] ? nodeq[0] : 0) * W) * 4u;
+  const uint32_t mrow1 = (uint32_t)((okq[1] ? nodeq[1] : 0) * W) * 4u;
 
   // per-lane LDS read offsets (see the reads below)
   int kofs[4];
@@ -500,6 +548,19 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     // waited for its own loads, and the stage refilled next was read one barrier ago
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __builtin_amdgcn_s_barrier();
+    // the tree split's mask words for this tile, issued ahead of the next tile's loads so
+    // that waiting for them leaves those in flight.  The tile's 64 keys span words wi and
+    // wi + 1; wi < W always (the tile starts below nn <= N), and when wi + 1 == W the
+    // second word's keys all lie past N, masked by the tail test, so it re-reads word wi.
+    uint32_t w[2][2];
+    if (tree) {
+      const uint32_t wi = (uint32_t)t * (kTile / 32);
+      const uint32_t wj = min(wi + 1, (uint32_t)W - 1);
+      w[0][0] = *(const uint32_t*)(mseq + (mrow0 + wi * 4));
+      w[0][1] = *(const uint32_t*)(mseq + (mrow0 + wj * 4));
+      w[1][0] = *(const uint32_t*)(mseq + (mrow1 + wi * 4));
+      w[1][1] = *(const uint32_t*)(mseq + (mrow1 + wj * 4));
+    }
     if (t + 1 < ntiles) issue.template operator()<ST ^ 1>(t + 1);
     if (!live) return;
 
@@ -516,33 +577,43 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     const unsigned char* Ks = ring_k<ST>();
     const unsigned char* Vs = ring_v<ST>();
     const int64_t t0 = lo + (int64_t)t * kTile;
-    const int rem = (int)(hi - lo) - t * kTile;  // keys left in the split; masks apply if < 64
+    const int rem = __builtin_amdgcn_readfirstlane((int)span - t * kTile);  // keys left; masks if < 64
 
-    // ---- S^T = K . Q^T  (4 key blocks x 2 query blocks).  Key kb4*16 + l16 has the
-    // swizzle of l16, so the lane's read offsets are kofs[kk] + kb4 * 4096.
+    // ---- S^T = K . Q^T  (4 key blocks x 2 query blocks), head-dim step kk outermost:
+    // eight independent accumulators per step, and step kk + 1's four K fragments are
+    // read while step kk's eight MFMAs run.  Key kb4*16 + l16 has the swizzle of l16, so
+    // the lane's read offsets are kofs[kk] + kb4 * 4096.
     f32x4 sacc[2][4];
+    bf16x8 kf[2][4];
+    auto kread = [&](int kk, bf16x8 (&f)[4]) {
 #pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      for (int kb4 = 0; kb4 < 4; ++kb4) f[kb4] = *reinterpret_cast<const bf16x8*>(Ks + kof[kk] + kb4 * 4096);
+    };
+    kread(0, kf[0]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kof[kk] + kb4 * 4096);
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) kread(kk + 1, kf[(kk + 1) & 1]);
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          sacc[qb][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][kk],
+          sacc[qb][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][kb4], qf[qb][kk],
                                                                   kk == 0 ? f32x4{} : sacc[qb][kb4], 0, 0, 0);
-      }
-      if (kb4 & 1) __builtin_amdgcn_sched_barrier(0);  // at most 8 K fragments live
     }
+    // order: the first two steps' reads, then per step two MFMAs per read of the next
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: bounded register use
     // ---- masks: ragged tail, and in the tree split the ancestor bits
     if (tree) {
       // bit (kin) of the two 32-key words; this lane's keys are kb4*16 + 4*g4 + r
-      const int wi = (int)(t0 >> 5);
-      uint32_t w[2][2];
-      w[0][0] = wi < W ? mrow0[wi] : 0u;
-      w[0][1] = wi + 1 < W ? mrow0[wi + 1] : 0u;
-      w[1][0] = wi < W ? mrow1[wi] : 0u;
-      w[1][1] = wi + 1 < W ? mrow1[wi + 1] : 0u;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -553,6 +624,7 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
             if (kb4 * 16 + g4 * 4 + r >= rem || !((bits >> r) & 1u)) sacc[qb][kb4][r] = -INFINITY;
         }
     } else if (rem < kTile) {
+      asm volatile("" ::: "memory");  // a real branch: taken on a split's last tile only
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
@@ -577,6 +649,9 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       need[qb] = tmax[qb] > m_run[qb] + kTau;   // always true on the first unmasked tile
     }
     if (ballot(need[0] || need[1])) {
+      // a real branch, taken rarely: left to itself the compiler runs this body on every
+      // tile as selects (74 multiplies per tile)
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float m_new = need[qb] ? tmax[qb] : m_run[qb];
@@ -602,8 +677,9 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     __builtin_amdgcn_sched_barrier(0);
     // ---- O^T += V^T . P^T  (V^T read transposed from the row-major tile).  The two
     // key rows a lane addresses (vrow, vrow + 16, plus 32 per key half) share one
-    // swizzle, so the chunk slot is (2 db) ^ vsw_hi | vsw_lo.
-    // The fragments of head-dim block db + 2 are read while block db's MFMAs run.
+    // swizzle, so the chunk slot is (2 db) ^ vsw_hi | vsw_lo.  Head-dim blocks go in
+    // pairs: a pair's eight MFMAs alternate four accumulators, and the next pair's eight
+    // fragment reads are issued while they run.
     auto vread = [&](int db, bf16x8 (&a)[2]) {
       const int slot = (((2 * db) ^ vhi) | vlo) << 4;
 #pragma unroll
@@ -614,26 +690,43 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
         a[kh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
-    bf16x8 va[3][2];
-    vread(0, va[0]);
-    vread(1, va[1]);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      if (db + 2 < 8) vread(db + 2, va[(db + 2) % 3]);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db % 3][kh], pb[qb][kh], oacc[qb][db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);  // V fragments of three blocks live at most
-    }
+    bf16x8 va[2][2][2];  // [buffer][db of the pair][kh]
+    vread(0, va[0][0]);
+    vread(1, va[0][1]);
     // sum_k P[k][q] for every query: the same contraction with V replaced by ones
-    // (the sum is of the bf16 weights the numerator uses)
+    // (the sum is of the bf16 weights the numerator uses); these cover the first reads
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
         lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][kh], lacc[qb], 0, 0, 0);
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      if (pr + 1 < 4) {
+        vread(2 * pr + 2, va[(pr + 1) & 1][0]);
+        vread(2 * pr + 3, va[(pr + 1) & 1][1]);
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            oacc[qb][2 * pr + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[pr & 1][j][kh], pb[qb][kh],
+                                                                            oacc[qb][2 * pr + j], 0, 0, 0);
+    }
+    // order: the first pair's reads, the row sums, then per pair one MFMA per read of
+    // the next pair
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+#pragma unroll
+    for (int pr = 0; pr < 3; ++pr)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
   };
 
   // prologue: tile 0 in flight.  Tile t uses stage t % 2; the loop is unrolled by the

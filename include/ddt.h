@@ -225,7 +225,9 @@ int ddt_adapt_budget(const float* cost, int S, int B, int32_t* tree_tok, int32_t
  * v_tree
  * mask       [S, N, W] from ddt_tree_mask; num_nodes [S]
  * dtype      DDT_F32 or DDT_BF16 for q, K, V and out; accumulation is fp32.
- * D          32, 64 or 128; Hq % Hkv == 0; scale finite and > 0.
+ * D          32, 64 or 128; Hq % Hkv == 0; scale finite and > 0.  For DDT_BF16,
+ *            64 key rows (64 * Hkv * D * 2 bytes) must span less than 2 GiB, else
+ *            DDT_ERR_UNSUPPORTED.
  * max_prefix host upper bound on every P_s: it sizes the key-split plan and the
  *            workspace.  A larger P_s is still computed correctly, more slowly.
  * out        [S, N, Hq, D] (dtype); rows n >= num_nodes[s] are written as 0.

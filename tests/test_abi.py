@@ -114,6 +114,9 @@ def test_attention_validation():
     assert call(scale=float("nan")) == -1
     assert call(maxp=-1) == -1
     assert call(B=1024) == -1
+    # bf16: 64 key rows of Hkv * D * 2 bytes must stay under 2 GiB (32-bit tile offsets)
+    assert call(Hq=1 << 17, Hkv=1 << 17, B=0) == -2
+    assert call(Hq=1 << 17, Hkv=1 << 17, B=0, dt=0, maxp=-1) == -1   # fp32: only the usual checks
 
 
 def test_adapt_budget_validation():
