@@ -19,6 +19,9 @@ What is synthesised, and why:
     elsewhere it is uniform.  All target randomness is keyed by the node's token
     path, so the target is a deterministic function of the path, as a real model
     conditioned on the same context would be.
+  * the target's last layer for the fused verifier epilogue: an LM-head weight
+    N(0, 1/d) and per-node final hidden states that plant the node's target token
+    (section "verifier epilogue" below).
 
 Seeds: numpy SeedSequence keyed by (workload id, sequence, [attempt], stream tag,
 ...).  ``attempt`` re-draws the draft side only; callers bump it to reject draws
@@ -116,9 +119,8 @@ def node_paths(tree_tok: np.ndarray, parent: np.ndarray, num_nodes: int) -> List
     return paths
 
 
-def target_row(cfg: Config, seq: int, attempt: int, path: Sequence[int],
-               chain: np.ndarray, keep: np.ndarray) -> np.ndarray:
-    """The synthetic target's next-token logits [V] fp32 after context b, *path."""
+def _target_draw(cfg: Config, seq: int, attempt: int, path: Sequence[int],
+                 chain: np.ndarray, keep: np.ndarray):
     d = len(path)
     r = _rng(cfg.cfg_id, seq, attempt, _T_TARGET, d, *[int(t) for t in path])
     row = r.standard_normal(cfg.V, dtype=np.float32)
@@ -127,8 +129,22 @@ def target_row(cfg: Config, seq: int, attempt: int, path: Sequence[int],
         tok = int(chain[d])
     else:
         tok = int(r.integers(0, cfg.V))
+    return row, tok
+
+
+def target_row(cfg: Config, seq: int, attempt: int, path: Sequence[int],
+               chain: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """The synthetic target's next-token logits [V] fp32 after context b, *path."""
+    row, tok = _target_draw(cfg, seq, attempt, path, chain, keep)
     row[tok] = np.float32(np.float64(row[tok]) + TARGET_BOOST)
     return row
+
+
+def target_token(cfg: Config, seq: int, attempt: int, path: Sequence[int],
+                 chain: np.ndarray, keep: np.ndarray) -> int:
+    """The token target_row lifts by TARGET_BOOST after context b, *path (the same
+    draws): the synthetic target's planted choice there."""
+    return _target_draw(cfg, seq, attempt, path, chain, keep)[1]
 
 
 def target_logits(cfg: Config, seq: int, attempt: int, tree_tok: np.ndarray, parent: np.ndarray,
@@ -297,3 +313,89 @@ def gumbel_noise(cfg: Config, seq: int, rnd: int = 0) -> np.ndarray:
     and the library take them as an input."""
     r = _rng(cfg.cfg_id, seq, _T_GUMBEL, rnd)
     return r.gumbel(size=(cfg.L + 1, cfg.V)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- verifier epilogue
+# The target's last layer at every tree node: a final hidden state h [d] and the LM
+# head (output embedding) W [V, d], both bfloat16, with d = Hq * D (the model width of
+# the workload's attention shape).  W is drawn N(0, 1/d), so an unplanted logit h . w_v
+# is about N(0, 1) for h ~ N(0, I).  A node's hidden state is z + beta * w_t with
+# z ~ N(0, I_d) and t a planted token: its logit for t is then about beta (|w_t|^2 is
+# about 1) against N(0, 1 + beta^2 / d) elsewhere, so with beta = 12 the planted
+# token leads the rest of a 128K vocabulary (whose maximum is about 4.9) by about 7.
+# A token < 0 plants nothing (h = z).  Rounded to bfloat16 (nearest even).
+_T_LMHEAD, _T_HIDDEN = 40, 41
+HIDDEN_BETA = 12.0
+LMHEAD_CHUNK = 4096  # vocabulary rows per seed chunk, so that threads can share the draw
+
+
+def d_model(cfg: Config) -> int:
+    return cfg.Hq * cfg.D
+
+
+def lm_head_weight(cfg: Config, d: Optional[int] = None, workers: int = 1) -> np.ndarray:
+    """LM-head weight [V, d] as bfloat16 encodings (uint16), N(0, 1/d), drawn in chunks
+    of LMHEAD_CHUNK vocabulary rows each with its own seed (the same array for any
+    ``workers``)."""
+    d = d_model(cfg) if d is None else int(d)
+    out = np.empty((cfg.V, d), dtype=np.uint16)
+    sd = np.float32(1.0 / np.sqrt(d))
+
+    def fill(c):
+        lo, hi = c * LMHEAD_CHUNK, min(cfg.V, (c + 1) * LMHEAD_CHUNK)
+        r = _rng(cfg.cfg_id, _T_LMHEAD, d, c)
+        out[lo:hi] = f32_to_bf16_bits(r.standard_normal((hi - lo, d), dtype=np.float32) * sd)
+
+    chunks = range((cfg.V + LMHEAD_CHUNK - 1) // LMHEAD_CHUNK)
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, chunks))
+    else:
+        for c in chunks:
+            fill(c)
+    return out
+
+
+def hidden_states(cfg: Config, seq: int, weight_bits: np.ndarray, tokens: Sequence[int],
+                  beta: float = HIDDEN_BETA, rnd: int = 0) -> np.ndarray:
+    """Final hidden states [len(tokens), d] (bfloat16 encodings) of one sequence's
+    nodes: row n is z_n + beta * w_{tokens[n]} (z_n ~ N(0, I_d) keyed by the
+    sequence, round and node), or z_n where tokens[n] < 0."""
+    d = weight_bits.shape[1]
+    n = len(tokens)
+    r = _rng(cfg.cfg_id, seq, _T_HIDDEN, rnd, d)
+    h = r.standard_normal((n, d), dtype=np.float32)
+    for i, t in enumerate(tokens):
+        if int(t) >= 0:
+            h[i] += np.float32(beta) * bf16_bits_to_f32(weight_bits[int(t)])
+    return f32_to_bf16_bits(h)
+
+
+def tree_hidden_states(cfg: Config, b: Dict[str, np.ndarray], tree: Dict[str, np.ndarray],
+                       weight_bits: np.ndarray, beta: float = HIDDEN_BETA,
+                       workers: int = 1) -> np.ndarray:
+    """Hidden states [S, N, d] for the trees of a batch: node n of sequence s plants
+    the synthetic target's token after n's path (target_token), so the argmax of the
+    LM head at every node is the token the target logits of ``target_logits`` lift.
+    ``tree`` holds tree_tok / parent / num_nodes [S, N] / [S]; padding rows plant
+    nothing."""
+    S, N, d = cfg.S, cfg.N, weight_bits.shape[1]
+    out = np.empty((S, N, d), dtype=np.uint16)
+    att = b.get("attempts", np.zeros(S, dtype=np.int64))
+
+    def fill(s):
+        nn = int(tree["num_nodes"][s])
+        toks = [-1] * N
+        for n, path in enumerate(node_paths(tree["tree_tok"][s], tree["parent"][s], nn)):
+            toks[n] = target_token(cfg, s, int(att[s]), path, b["chain"][s], b["keep"][s])
+        out[s] = hidden_states(cfg, s, weight_bits, toks, beta)
+
+    if workers > 1 and S > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(workers, S)) as ex:
+            list(ex.map(fill, range(S)))
+    else:
+        for s in range(S):
+            fill(s)
+    return out

@@ -9,5 +9,8 @@ from .ddtree import (  # noqa: F401
     selection_gap, softmax_topk_row,
     topk, tree_attention, tree_mask, tree_walk, tree_walk_sample, visible_nodes,
 )
+from .epilogue import (  # noqa: F401
+    fp32_accumulation_bound, lm_head_argmax, lm_head_logits, top_two, tree_walk_tokens,
+)
 from .round import verify_round  # noqa: F401
 from .rounds import commit_kv, greedy_decode, run_rounds  # noqa: F401
