@@ -57,6 +57,11 @@ def load() -> ctypes.CDLL:
                                        vp, sz, vp]),
         "ddt_tree_walk_noalloc_max_bytes": (sz, []),
         "ddt_tree_walk_noalloc": (i32, [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp]),
+        "ddt_lm_head_argmax_workspace_size": (sz, [i32, i32, i64, i32]),
+        "ddt_lm_head_argmax": (i32, [vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, sz, vp]),
+        "ddt_tree_walk_tokens": (i32, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "ddt_lm_head_profiling": (i32, [i32]),
+        "ddt_lm_head_timing": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
         "ddt_attention_profiling": (i32, [i32]),
         "ddt_attention_timing": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int)]),
@@ -75,7 +80,9 @@ EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_buil
            "ddt_commit_kv",
            "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_tree_walk_sample",
            "ddt_tree_walk_noalloc_max_bytes",
-           "ddt_tree_walk_noalloc", "ddt_attention_profiling", "ddt_attention_timing")
+           "ddt_tree_walk_noalloc", "ddt_lm_head_argmax_workspace_size", "ddt_lm_head_argmax",
+           "ddt_tree_walk_tokens", "ddt_lm_head_profiling", "ddt_lm_head_timing",
+           "ddt_attention_profiling", "ddt_attention_timing")
 
 
 def _check(status: int, what: str):
@@ -386,6 +393,68 @@ def ddt_tree_walk_noalloc(tree_tok, parent, num_nodes, target_logits, L: int, ou
                                      _p(out["acc_tok"]), _p(out["bonus"]), _stream(dev)),
            "ddt_tree_walk_noalloc")
     return out
+
+
+def ddt_lm_head_argmax(hidden, weight, num_nodes=None, out_tok=None, out_max=None, ws=None,
+                       with_max: bool = True):
+    """hidden [S, N, d] bf16, weight [V, d] bf16 -> (node_tok [S, N] int32, node_max [S, N]
+    fp32 or None): the LM-head arg-max per node, equal logits to the smaller id."""
+    lib = load()
+    _dev(hidden, "hidden", torch.bfloat16)
+    _dev(weight, "weight", torch.bfloat16)
+    if hidden.dim() != 3 or weight.dim() != 2 or hidden.shape[2] != weight.shape[1]:
+        raise ValueError("hidden must be [S, N, d] and weight [V, d]")
+    S, N, d = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    if num_nodes is not None:
+        _dev(num_nodes, "num_nodes", torch.int32, (S,))
+    if out_tok is None:
+        out_tok = torch.empty(S, N, dtype=torch.int32, device=dev)
+    _dev(out_tok, "out_tok", torch.int32, (S, N))
+    if out_max is None and with_max:
+        out_max = torch.empty(S, N, dtype=torch.float32, device=dev)
+    if out_max is not None:
+        _dev(out_max, "out_max", torch.float32, (S, N))
+    need = lib.ddt_lm_head_argmax_workspace_size(S, N - 1, V, d)
+    if ws is None:
+        ws = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    _check(lib.ddt_lm_head_argmax(_p(hidden), _p(weight), _p(num_nodes), S, N - 1, d, V,
+                                  _p(out_tok), _p(out_max), _p(ws), ws.numel(), _stream(dev)),
+           "ddt_lm_head_argmax")
+    return out_tok, out_max
+
+
+def ddt_tree_walk_tokens(tree_tok, parent, num_nodes, node_tok, L: int, out=None):
+    """node_tok [S, N] int32 (each node's target token) -> dict(accept_len [S],
+    acc_nodes [S, L], acc_tok [S, L], bonus [S])."""
+    lib = load()
+    S, N = tree_tok.shape
+    _dev(tree_tok, "tree_tok", torch.int32)
+    _dev(parent, "parent", torch.int32, (S, N))
+    _dev(num_nodes, "num_nodes", torch.int32, (S,))
+    _dev(node_tok, "node_tok", torch.int32, (S, N))
+    dev = tree_tok.device
+    if out is None:
+        out = {"accept_len": torch.empty(S, dtype=torch.int32, device=dev),
+               "acc_nodes": torch.empty(S, L, dtype=torch.int32, device=dev),
+               "acc_tok": torch.empty(S, L, dtype=torch.int32, device=dev),
+               "bonus": torch.empty(S, dtype=torch.int32, device=dev)}
+    _check(lib.ddt_tree_walk_tokens(_p(tree_tok), _p(parent), _p(num_nodes), _p(node_tok), S, N - 1,
+                                    L, _p(out["accept_len"]), _p(out["acc_nodes"]), _p(out["acc_tok"]),
+                                    _p(out["bonus"]), _stream(dev)), "ddt_tree_walk_tokens")
+    return out
+
+
+def lm_head_profiling(enable: bool):
+    _check(load().ddt_lm_head_profiling(1 if enable else 0), "ddt_lm_head_profiling")
+
+
+def lm_head_timing() -> Tuple[float, int]:
+    """(summed milliseconds of the epilogue's tile kernel, calls) since the last read."""
+    tm, n = ctypes.c_double(0.0), ctypes.c_int(0)
+    _check(load().ddt_lm_head_timing(ctypes.byref(tm), ctypes.byref(n)), "ddt_lm_head_timing")
+    return tm.value, n.value
 
 
 def attention_profiling(enable: bool):

@@ -40,14 +40,13 @@ struct Prof {
   std::vector<ProfEvents> pool;
   size_t used = 0;
 };
-Prof& prof() {
-  static Prof p;
-  return p;
+// one pool per timed kernel: the attention's main kernel, the epilogue's tile kernel
+Prof& prof(int which = 0) {
+  static Prof p[2];
+  return p[which];
 }
-}  // namespace
 
-bool prof_events(hipEvent_t* start, hipEvent_t* stop, hipEvent_t* step_stop) {
-  Prof& p = prof();
+bool take_events(Prof& p, hipEvent_t* start, hipEvent_t* stop, hipEvent_t* step_stop) {
   std::lock_guard<std::mutex> lk(p.mu);
   if (!p.on) return false;
   if (p.used == p.pool.size()) {
@@ -66,6 +65,54 @@ bool prof_events(hipEvent_t* start, hipEvent_t* stop, hipEvent_t* step_stop) {
   *stop = e.stop;
   if (step_stop) *step_stop = e.step_stop;
   return true;
+}
+
+int set_profiling(Prof& p, int enable) {
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.on = enable != 0;
+  if (!p.on) {
+    int rc = DDT_OK;
+    for (auto& ev : p.pool)
+      for (hipEvent_t e : {ev.start, ev.stop, ev.step_stop})
+        if (hipEventDestroy(e) != hipSuccess) rc = DDT_ERR_HIP;
+    p.pool.clear();
+    p.used = 0;
+    return rc;
+  }
+  return DDT_OK;
+}
+
+// sums of the recorded (start, stop) and (start, step stop) intervals since the last
+// read, and their count
+int read_timing(Prof& p, double* main_ms, double* step_ms, int* count) {
+  std::lock_guard<std::mutex> lk(p.mu);
+  double tm = 0.0, ts = 0.0;
+  int n = 0;
+  for (size_t i = 0; i < p.used; ++i) {
+    const ProfEvents& e = p.pool[i];
+    const hipEvent_t last = e.step_used ? e.step_stop : e.stop;
+    if (hipEventSynchronize(last) != hipSuccess) return DDT_ERR_HIP;
+    float a = 0.f, b = 0.f;
+    if (hipEventElapsedTime(&a, e.start, e.stop) != hipSuccess) return DDT_ERR_HIP;
+    if (hipEventElapsedTime(&b, e.start, last) != hipSuccess) return DDT_ERR_HIP;
+    tm += a;
+    ts += b;
+    ++n;
+  }
+  p.used = 0;
+  *main_ms = tm;
+  if (step_ms) *step_ms = ts;
+  *count = n;
+  return DDT_OK;
+}
+}  // namespace
+
+bool prof_events(hipEvent_t* start, hipEvent_t* stop, hipEvent_t* step_stop) {
+  return take_events(prof(0), start, stop, step_stop);
+}
+
+bool lm_prof_events(hipEvent_t* start, hipEvent_t* stop) {
+  return take_events(prof(1), start, stop, nullptr);
 }
 
 }  // namespace ddt
@@ -258,6 +305,41 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                                      as_stream(stream)));
 }
 
+size_t ddt_lm_head_argmax_workspace_size(int S, int B, int64_t vocab, int d) {
+  if (S < 1 || B < 0 || B > DDT_MAX_B || vocab < 1 || vocab > INT32_MAX - 512 || d < 64 ||
+      d > 65536 || d % 64 != 0)
+    return 0;
+  return lm_head_plan(S, B, vocab, d).ws_bytes;
+}
+
+int ddt_lm_head_argmax(const void* hidden, const void* weight, const int32_t* num_nodes, int S,
+                       int B, int d, int64_t vocab, int32_t* node_tok, float* node_max, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!hidden || !weight || !node_tok) return DDT_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(hidden) % 16 != 0 || reinterpret_cast<uintptr_t>(weight) % 16 != 0)
+    return DDT_ERR_INVALID_ARG;
+  if (S < 1 || B < 0 || B > DDT_MAX_B || vocab < 1 || vocab > INT32_MAX - 512 || d < 64 || d > 65536)
+    return DDT_ERR_INVALID_ARG;
+  if (d % 64 != 0) return DDT_ERR_UNSUPPORTED;
+  if ((int64_t)S * (B + 1) * ((vocab + 255) / 256) > INT32_MAX) return DDT_ERR_UNSUPPORTED;
+  const LmPlan plan = lm_head_plan(S, B, vocab, d);
+  if (!ws || ws_bytes < plan.ws_bytes) return DDT_ERR_WORKSPACE;
+  return hip_status(launch_lm_head(hidden, weight, num_nodes, S, B, d, vocab, node_tok, node_max,
+                                   ws, plan, as_stream(stream)));
+}
+
+int ddt_tree_walk_tokens(const int32_t* tree_tok, const int32_t* parent, const int32_t* num_nodes,
+                         const int32_t* node_tok, int S, int B, int L, int32_t* accept_len,
+                         int32_t* acc_nodes, int32_t* acc_tok, int32_t* bonus_out, void* stream) {
+  if (!tree_tok || !parent || !num_nodes || !node_tok || !accept_len || !acc_nodes || !acc_tok ||
+      !bonus_out)
+    return DDT_ERR_INVALID_ARG;
+  if (S < 1 || L < 1 || L > DDT_MAX_L || B < 0 || B > DDT_MAX_B) return DDT_ERR_INVALID_ARG;
+  return hip_status(launch_tree_walk_tokens(tree_tok, parent, num_nodes, node_tok, S, B, L,
+                                            accept_len, acc_nodes, acc_tok, bonus_out,
+                                            as_stream(stream)));
+}
+
 int ddt_tree_walk_sample(const int32_t* tree_tok, const int32_t* parent, const int32_t* depth,
                          const int32_t* num_nodes, const float* target_logits, const float* gumbel,
                          float inv_temperature, int S, int B, int L, int64_t vocab,
@@ -297,44 +379,18 @@ int ddt_tree_walk_noalloc(const int32_t* tree_tok, const int32_t* parent, const 
 size_t ddt_tree_walk_noalloc_max_bytes(void) { return walk_scratch_bytes(); }
 
 // ------------------------------------------------------------------ benchmark aid
-int ddt_attention_profiling(int enable) {
-  Prof& p = prof();
-  std::lock_guard<std::mutex> lk(p.mu);
-  p.on = enable != 0;
-  if (!p.on) {
-    int rc = DDT_OK;
-    for (auto& ev : p.pool)
-      for (hipEvent_t e : {ev.start, ev.stop, ev.step_stop})
-        if (hipEventDestroy(e) != hipSuccess) rc = DDT_ERR_HIP;
-    p.pool.clear();
-    p.used = 0;
-    return rc;
-  }
-  return DDT_OK;
-}
+int ddt_attention_profiling(int enable) { return set_profiling(prof(0), enable); }
 
 int ddt_attention_timing(double* main_ms, double* step_ms, int* count) {
   if (!main_ms || !step_ms || !count) return DDT_ERR_INVALID_ARG;
-  Prof& p = prof();
-  std::lock_guard<std::mutex> lk(p.mu);
-  double tm = 0.0, ts = 0.0;
-  int n = 0;
-  for (size_t i = 0; i < p.used; ++i) {
-    const ProfEvents& e = p.pool[i];
-    const hipEvent_t last = e.step_used ? e.step_stop : e.stop;
-    if (hipEventSynchronize(last) != hipSuccess) return DDT_ERR_HIP;
-    float a = 0.f, b = 0.f;
-    if (hipEventElapsedTime(&a, e.start, e.stop) != hipSuccess) return DDT_ERR_HIP;
-    if (hipEventElapsedTime(&b, e.start, last) != hipSuccess) return DDT_ERR_HIP;
-    tm += a;
-    ts += b;
-    ++n;
-  }
-  p.used = 0;
-  *main_ms = tm;
-  *step_ms = ts;
-  *count = n;
-  return DDT_OK;
+  return read_timing(prof(0), main_ms, step_ms, count);
+}
+
+int ddt_lm_head_profiling(int enable) { return set_profiling(prof(1), enable); }
+
+int ddt_lm_head_timing(double* tiles_ms, int* count) {
+  if (!tiles_ms || !count) return DDT_ERR_INVALID_ARG;
+  return read_timing(prof(1), tiles_ms, nullptr, count);
 }
 
 }  // extern "C"

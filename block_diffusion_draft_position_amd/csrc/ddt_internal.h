@@ -242,6 +242,25 @@ hipError_t launch_commit_kv(void* k_cache, void* v_cache, const int64_t* cu_pref
                             const int32_t* acc_nodes, const int32_t* accept_len, int S, int N,
                             int L, int64_t row_bytes, int32_t* appended, hipStream_t st);
 
+// verifier epilogue: LM head + arg-max per hidden row (partials per vocabulary tile in
+// ws, then a per-row reduce), and the tree walk driven by the resulting tokens
+struct LmPlan {
+  int vt, mt;       // tile: vocabulary rows x hidden rows
+  int nvt;          // vocabulary tiles
+  size_t ws_bytes;  // partials [S * N, nvt] (value, id)
+};
+LmPlan lm_head_plan(int S, int B, int64_t vocab, int d);
+hipError_t launch_lm_head(const void* hidden, const void* weight, const int32_t* num_nodes, int S,
+                          int B, int d, int64_t vocab, int32_t* node_tok, float* node_max,
+                          void* ws, const LmPlan& p, hipStream_t st);
+hipError_t launch_tree_walk_tokens(const int32_t* tree_tok, const int32_t* parent,
+                                   const int32_t* num_nodes, const int32_t* node_tok, int S, int B,
+                                   int L, int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok,
+                                   int32_t* bonus_out, hipStream_t st);
+// Benchmark timing of the epilogue's tile kernel: as prof_events, one start/stop pair
+// per launch while epilogue profiling is on.
+bool lm_prof_events(hipEvent_t* start, hipEvent_t* stop);
+
 // Benchmark timing of the attention's main kernel and of the whole attention step
 // (see ddt_attention_profiling).  While profiling is on, prof_events hands out a
 // start/stop event pair that the launch attaches to the main kernel's dispatch

@@ -347,6 +347,45 @@ int ddt_tree_walk_noalloc(const int32_t* tree_tok, const int32_t* parent, const 
                           int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok,
                           int32_t* bonus_out, void* stream);
 
+/* ---------------------------------------------------------------- verifier epilogue
+ * The target's last layer and greedy choice at every tree node without storing the
+ * logits: the tree is scored in one target forward (運作流程 step 3) and the walk
+ * needs only each node's greedy token (step 4).  Node n's logits are its final hidden
+ * state times the LM-head weight, logit_v = h_n . w_v, and its token is their
+ * arg-max, equal values to the smaller id.
+ *
+ * hidden     [S, N, d] bf16 (N = B + 1), 16-byte aligned: final hidden states.
+ * weight     [V, d] bf16 (V = vocab), 16-byte aligned: one row per vocabulary entry.
+ * num_nodes  nullable [S]: nodes n >= num_nodes[s] are padding (token -1, max -inf);
+ *            every row is still multiplied, so padding rows must hold finite values
+ *            or their (unused) products may be anything.
+ * node_tok   [S, N] int32 out: arg-max_v of the fp32 logits (bf16 products, fp32 sums).
+ * node_max   nullable [S, N] fp32 out: that logit.
+ * d          multiple of 64, 64 <= d <= 65536; 1 <= vocab <= 2^31 - 512;
+ *            1 <= S, 0 <= B <= DDT_MAX_B.  Logits must not overflow fp32.
+ * ws         at least ddt_lm_head_argmax_workspace_size(S, B, vocab, d) bytes: the
+ *            partial arg-max of each (node, 256-entry vocabulary tile).  Contents are
+ *            ignored.
+ * Errors: null required pointer, unaligned hidden or weight, size out of range
+ *         (DDT_ERR_INVALID_ARG); d not a multiple of 64 (DDT_ERR_UNSUPPORTED); ws_bytes
+ *         too small (DDT_ERR_WORKSPACE).
+ */
+size_t ddt_lm_head_argmax_workspace_size(int S, int B, int64_t vocab, int d);
+int ddt_lm_head_argmax(const void* hidden, const void* weight, const int32_t* num_nodes, int S,
+                       int B, int d, int64_t vocab, int32_t* node_tok, float* node_max, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Tree walk of 運作流程 step 4 driven by given per-node target tokens (from
+ * ddt_lm_head_argmax): from the root, while a child of the current node (the smallest
+ * index first) carries the current node's token, accept it and move there; the token
+ * at the node where the walk stops is the next round's bonus.  Inputs and outputs as
+ * ddt_tree_walk, with node_tok [S, N] int32 in place of the logits.
+ * Errors: null pointer; S < 1; L outside [1, DDT_MAX_L]; B outside [0, DDT_MAX_B].
+ */
+int ddt_tree_walk_tokens(const int32_t* tree_tok, const int32_t* parent, const int32_t* num_nodes,
+                         const int32_t* node_tok, int S, int B, int L, int32_t* accept_len,
+                         int32_t* acc_nodes, int32_t* acc_tok, int32_t* bonus_out, void* stream);
+
 /* ---------------------------------------------------------------- benchmark aid
  * Timing of the attention step (the round's dominant cost) with HIP events on the
  * stream it runs on.  While profiling is on, every ddt_tree_attention call attaches
@@ -363,6 +402,14 @@ int ddt_tree_walk_noalloc(const int32_t* tree_tok, const int32_t* parent, const 
  */
 int ddt_attention_profiling(int enable);
 int ddt_attention_timing(double* main_ms, double* step_ms, int* count);
+
+/* The same for the verifier epilogue's tile kernel (the LM-head product and the
+ * per-tile arg-max; the per-node reduce that follows is not included):
+ * ddt_lm_head_timing returns the summed milliseconds and the count of the recorded
+ * ddt_lm_head_argmax calls since the last read.  Same rules and errors as above.
+ */
+int ddt_lm_head_profiling(int enable);
+int ddt_lm_head_timing(double* tiles_ms, int* count);
 
 #ifdef __cplusplus
 }

@@ -194,3 +194,34 @@ def test_product_path_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libddt.so")
     with pytest.raises(_lib.DDTError):
         _lib.load()
+
+
+def test_lm_head_validation():
+    lib = ddt.load()
+    f = lib.ddt_lm_head_argmax
+    a = [_fake(16 * i) for i in range(1, 12)]
+
+    def call(S=1, B=8, d=128, V=1000, h=a[0], w=a[1], tok=a[2], ws_bytes=1 << 20):
+        return f(h, w, None, S, B, d, V, tok, None, a[3], ws_bytes, None)
+    assert call(h=None) == -1
+    assert call(tok=None) == -1
+    assert call(h=ctypes.c_void_p(0x10008)) == -1   # unaligned hidden
+    assert call(w=ctypes.c_void_p(0x20004)) == -1   # unaligned weight
+    assert call(S=0) == -1
+    assert call(B=1024) == -1
+    assert call(V=0) == -1
+    assert call(d=32) == -1                 # below one K-step
+    assert call(d=96) == -2                 # not a multiple of 64
+    assert call(ws_bytes=8) == -3           # workspace too small
+    assert lib.ddt_lm_head_argmax_workspace_size(1, 8, 1000, 96) == 0
+    assert lib.ddt_lm_head_argmax_workspace_size(2, 8, 1000, 128) >= 2 * 9 * 4 * 8
+
+
+def test_walk_tokens_validation():
+    f = ddt.load().ddt_tree_walk_tokens
+    a = [_fake(i) for i in range(1, 12)]
+    assert f(None, a[1], a[2], a[3], 1, 8, 4, a[4], a[5], a[6], a[7], None) == -1
+    assert f(a[0], a[1], a[2], None, 1, 8, 4, a[4], a[5], a[6], a[7], None) == -1
+    assert f(a[0], a[1], a[2], a[3], 0, 8, 4, a[4], a[5], a[6], a[7], None) == -1
+    assert f(a[0], a[1], a[2], a[3], 1, 8, 0, a[4], a[5], a[6], a[7], None) == -1
+    assert f(a[0], a[1], a[2], a[3], 1, 1024, 4, a[4], a[5], a[6], a[7], None) == -1
