@@ -11,11 +11,16 @@
 // lm_head_tiles<VT, MT, NWV, NWM>: one workgroup per VT x MT tile of the logits
 // (vocabulary x hidden rows), K = d in steps of 64.
 //   * W and H tiles go global -> LDS by buffer_load_dwordx4 ... lds (no registers in
-//     between) into a 2-stage ring: step s + 1 is issued right after the barrier that
-//     opens step s.  An LDS row is one tile row's 64 K-values, 128 bytes in eight
-//     16-byte slots; chunk c of row r sits in slot c ^ ((r >> 1) & 7), so that the 16
-//     rows a 16-lane group reads in one fragment load fall in 16 distinct 16-byte
-//     bank groups.
+//     between) into a ring of NS stages (3 for the 256 x 128 tile: 144 KB, one
+//     workgroup per CU; 2 for the narrow tiles).  An LDS row is one tile row's 64
+//     K-values, 128 bytes in eight 16-byte slots; chunk c of row r sits in slot
+//     c ^ ((r >> 1) & 7), so that the 16 rows a 16-lane group reads in one fragment
+//     load fall in 16 distinct 16-byte bank groups (measured: no bank conflicts).
+//   * One barrier per K-step, placed before the step's last substep: by then each wave
+//     holds that substep's fragments in registers, so the stage can be refilled, and
+//     having waited for its own loads of the next step, the next step's first
+//     fragments are read while the last substep's MFMAs run.  Within a step each
+//     substep's MFMAs are interleaved with the next substep's fragment reads.
 //   * Logits^T tiles on v_mfma_f32_32x32x16_bf16 with the vocabulary rows as the A
 //     operand and the hidden rows as B: a lane's accumulators then hold one hidden row
 //     (its column) against 16 vocabulary rows, so the arg-max is in-lane first.
@@ -51,7 +56,7 @@ __device__ __forceinline__ int64_t rfl64(int64_t v) {
   return (int64_t)(((uint64_t)(uint32_t)hi32 << 32) | (uint32_t)lo32);
 }
 
-template <int VT, int MT, int NWV, int NWM>
+template <int VT, int MT, int NWV, int NWM, int NS>
 struct LmCfg {
   static constexpr int NW = NWV * NWM;
   static constexpr int VW = VT / NWV;            // vocabulary rows per wave
@@ -59,19 +64,21 @@ struct LmCfg {
   static constexpr int VB = VW / 32;             // 32-row MFMA blocks
   static constexpr int MB = MW / 32;
   static constexpr int STAGE = (VT + MT) * kRowBytes;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = NS * STAGE;
   static constexpr int NINST = (VT + MT) / 8;    // 1 KB loads per stage (8 rows each)
   static constexpr int PER_WAVE = NINST / NW;
   static_assert(VW % 32 == 0 && MW % 32 == 0, "32-row blocks");
   static_assert(NINST % NW == 0, "loads deal evenly to the waves");
   static_assert(NWV * MT * (int)sizeof(Partial) <= LDS, "epilogue fits the ring");
+  static_assert(NS == 2 || NS == 3, "ring stages");
+  static_assert(PER_WAVE < 64, "vmcnt range");
 };
 
-template <int VT, int MT, int NWV, int NWM>
-__global__ void __launch_bounds__(NWV * NWM * 64, (2 * (VT + MT) * kRowBytes <= 81920 ? 2 : 1))
+template <int VT, int MT, int NWV, int NWM, int NS>
+__global__ void __launch_bounds__(NWV * NWM * 64, (NS * (VT + MT) * kRowBytes <= 81920 ? 2 : 1))
 lm_head_tiles(const bf16_t* __restrict__ H, const bf16_t* __restrict__ Wt, int M, int V, int d,
               int nvt, int nmt, int per_xcd, Partial* __restrict__ partial) {
-  using C = LmCfg<VT, MT, NWV, NWM>;
+  using C = LmCfg<VT, MT, NWV, NWM, NS>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
 
   // tiles are dealt to the eight XCDs (workgroup i runs on XCD i % 8) in contiguous
@@ -148,37 +155,79 @@ lm_head_tiles(const bf16_t* __restrict__ H, const bf16_t* __restrict__ Wt, int M
   // slot is (2 ks + h2) ^ ((l % 32 >> 1) & 7); the block bases are multiples of 32
   const int frag_base = l32 * kRowBytes;
   const int fsw = (l32 >> 1) & 7;
-  auto step = [&]<int ST>(int s) {
-    // this wave's loads of step s are the only ones in flight: wait for them, then a
-    // barrier (every wave has its step-s rows, and every wave is done reading the stage
-    // that the next issue refills)
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __builtin_amdgcn_s_barrier();
-    if (s + 1 < nk) issue.template operator()<ST ^ 1>(s + 1);
+  bf16x8 fa[2][C::VB], fb[2][C::MB];
+  auto rd = [&]<int ST, int KS, int BUF>() {
     const unsigned char* As = smem + ST * C::STAGE + (wv * C::VW) * kRowBytes + frag_base;
     const unsigned char* Bs = smem + ST * C::STAGE + (VT + wm * C::MW) * kRowBytes + frag_base;
+    const int slot = (((2 * KS + h2) ^ fsw) << 4);
 #pragma unroll
-    for (int ks = 0; ks < kKStep / 16; ++ks) {
-      const int slot = (((2 * ks + h2) ^ fsw) << 4);
-      bf16x8 a[C::VB], b[C::MB];
+    for (int vb = 0; vb < C::VB; ++vb)
+      fa[BUF][vb] = *reinterpret_cast<const bf16x8*>(As + vb * 32 * kRowBytes + slot);
 #pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb)
-        a[vb] = *reinterpret_cast<const bf16x8*>(As + vb * 32 * kRowBytes + slot);
+    for (int mb = 0; mb < C::MB; ++mb)
+      fb[BUF][mb] = *reinterpret_cast<const bf16x8*>(Bs + mb * 32 * kRowBytes + slot);
+  };
+  auto mfmas = [&]<int BUF>() {
+#pragma unroll
+    for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
-        b[mb] = *reinterpret_cast<const bf16x8*>(Bs + mb * 32 * kRowBytes + slot);
+        acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUF][vb], fb[BUF][mb], acc[vb][mb], 0, 0, 0);
+  };
+  // the reads of the next substep between this substep's MFMAs, one after each MFMA
+  auto interleave = [&]() {
 #pragma unroll
-      for (int vb = 0; vb < C::VB; ++vb)
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-          acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vb], b[mb], acc[vb][mb], 0, 0, 0);
+    for (int i = 0; i < C::VB + C::MB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, C::VB * C::MB - (C::VB + C::MB), 0);
+  };
+  // vmcnt(n) with the other counters left at their maxima
+  constexpr int kWaitOne = 0x0f70 | (C::PER_WAVE & 15) | ((C::PER_WAVE >> 4) << 14);
+
+  // Step s of stage ST (= s mod NS): substeps 0..2 each run their MFMAs with the next
+  // substep's fragments read in between.  Then, with substep 3's fragments in
+  // registers, the wave waits for its loads of step s + 1 and meets the barrier: every
+  // wave then holds what it needs of stage ST, which is refilled with step s + NS, and
+  // step s + 1's rows are visible, so its first fragments are read while substep 3's
+  // MFMAs run.
+  auto step = [&]<int ST>(int s) {
+    rd.template operator()<ST, 1, 1>();
+    mfmas.template operator()<0>();
+    interleave();
+    rd.template operator()<ST, 2, 0>();
+    mfmas.template operator()<1>();
+    interleave();
+    rd.template operator()<ST, 3, 1>();
+    mfmas.template operator()<0>();
+    interleave();
+    if (s + 1 < nk) {
+      if (NS == 3 && s + 2 < nk)
+        __builtin_amdgcn_s_waitcnt(kWaitOne & ~0x0f00);   // lgkmcnt(0), vmcnt(PER_WAVE)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0070);               // lgkmcnt(0), vmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      if (s + NS < nk) issue.template operator()<ST>(s + NS);
+      rd.template operator()<(ST + 1) % NS, 0, 0>();
+    }
+    mfmas.template operator()<1>();
   };
 
+  // prologue: the first NS steps in flight, then step 0's rows
   issue.template operator()<0>(0);
-  for (int s = 0; s < nk; s += 2) {
+  if (1 < nk) issue.template operator()<1 % NS>(1);
+  if (NS == 3 && 2 < nk) issue.template operator()<2 % NS>(2);
+  const int later = min(NS - 1, nk - 1);
+  if (later == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+  else if (later == 1) __builtin_amdgcn_s_waitcnt(kWaitOne);
+  else __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * C::PER_WAVE) & 15) | (((2 * C::PER_WAVE) >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  rd.template operator()<0, 0, 0>();
+  for (int s = 0; s < nk; s += NS) {
     step.template operator()<0>(s);
-    if (s + 1 < nk) step.template operator()<1>(s + 1);
+    if (s + 1 < nk) step.template operator()<1 % NS>(s + 1);
+    if (NS == 3 && s + 2 < nk) step.template operator()<2 % NS>(s + 2);
   }
 
   // ---- epilogue.  Lane l holds, for column block mb, hidden row wm*MW + mb*32 + l%32
@@ -295,13 +344,13 @@ tree_walk_tokens_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __r
   }
 }
 
-template <int VT, int MT, int NWV, int NWM>
+template <int VT, int MT, int NWV, int NWM, int NS>
 hipError_t launch_tiles(const void* H, const void* W, int M, int V, int d, Partial* part,
                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  using C = LmCfg<VT, MT, NWV, NWM>;
+  using C = LmCfg<VT, MT, NWV, NWM, NS>;
   const int nvt = (int)ceil_div(V, VT), nmt = (int)ceil_div(M, MT);
   const int per_xcd = (int)ceil_div((int64_t)nvt * nmt, 8);
-  hipExtLaunchKernelGGL((lm_head_tiles<VT, MT, NWV, NWM>), dim3(8 * per_xcd), dim3(C::NW * 64), 0,
+  hipExtLaunchKernelGGL((lm_head_tiles<VT, MT, NWV, NWM, NS>), dim3(8 * per_xcd), dim3(C::NW * 64), 0,
                         st, ev0, ev1, 0, (const bf16_t*)H, (const bf16_t*)W, M, V, d, nvt, nmt,
                         per_xcd, part);
   return hipGetLastError();
@@ -331,9 +380,9 @@ hipError_t launch_lm_head(const void* hidden, const void* weight, const int32_t*
   if (!lm_prof_events(&ev0, &ev1)) ev0 = ev1 = nullptr;
   hipError_t e;
   switch (p.mt) {
-    case 128: e = launch_tiles<256, 128, 2, 2>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
-    case 64: e = launch_tiles<256, 64, 4, 1>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
-    default: e = launch_tiles<256, 32, 4, 1>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
+    case 128: e = launch_tiles<256, 128, 2, 2, 3>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
+    case 64: e = launch_tiles<256, 64, 4, 1, 2>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
+    default: e = launch_tiles<256, 32, 4, 1, 2>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lm_head_reduce, dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, st, part, M, N,
