@@ -11,8 +11,9 @@ Hq = 64, Hkv = 8, D = 128, bf16.
 
 Prints one JSON line: rounds/s, the attention main kernel's roofline (HIP events
 attached to its dispatches), the whole attention step (main kernel and split merge)
-next to it, and the CPU oracle's rate on a bounded sample of the same workload,
-timed on this host's cores.
+next to it, the fused verifier epilogue (LM head + arg-max per node, on the same
+trees) with its own roofline, and the CPU oracle's rate on a bounded sample of the
+same workload, timed on this host's cores.
 """
 import argparse
 import json
@@ -100,18 +101,22 @@ def attention_kernel(cfg):
     return "attn_d128" if cfg.D == 128 else "attn_partial_bf16"
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_hbm_traffic.txt")
-ATTN_SOURCE = os.path.join(ROOT, "block_diffusion_draft_position_amd", "csrc", "tree_attention.hip")
+CSRC = os.path.join(ROOT, "block_diffusion_draft_position_amd", "csrc")
+TRAFFIC = {  # kernel -> (committed rocprofv3 summary, the source it was taken on)
+    "attention": (os.path.join(ROOT, "profiles", "attn_hbm_traffic.txt"), os.path.join(CSRC, "tree_attention.hip")),
+    "epilogue": (os.path.join(ROOT, "profiles", "lm_head_hbm_traffic.txt"), os.path.join(CSRC, "lm_head.hip")),
+}
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the attention main kernel, from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current kernel source."""
+def measured_traffic(workload, kernel="attention"):
+    """HBM bytes per launch of the kernel, from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, if it was taken on the current kernel source."""
     import hashlib
+    path, source = TRAFFIC[kernel]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
-        with open(ATTN_SOURCE, "rb") as f:
+        with open(source, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
@@ -123,6 +128,63 @@ def measured_traffic(workload):
             kv = dict(zip(l[2::2], l[3::2]))
             return float(kv["traffic_bytes"])
     return None
+
+
+def epilogue_bench(cfg, b, rnd, dev, up, workers, calls=20):
+    """The fused verifier epilogue on this workload's trees (the ones the timed rounds
+    build): final hidden states [S, N, Hq*D] that plant each node's synthetic target
+    token, an N(0, 1/d) LM-head weight [V, Hq*D], bf16.  Timed with HIP events attached
+    to the tile kernel's dispatches over eager calls; the walk from its tokens is
+    checked against the round's walk over the target logits."""
+    import torch
+    import block_diffusion_draft_position_amd as ddt
+    d = gen.d_model(cfg)
+    t0 = time.time()
+    W = gen.lm_head_weight(cfg, workers=workers)
+    tree = {k: rnd.tree[k].cpu().numpy() for k in ("tree_tok", "parent", "num_nodes")}
+    H = gen.tree_hidden_states(cfg, b, tree, W, workers=workers)
+    log(f"[bench] epilogue inputs ready in {time.time() - t0:.1f}s")
+    Wd, Hd = up(W), up(H)
+    del W, H
+    nn = rnd.tree["num_nodes"]
+    tok = torch.empty(cfg.S, cfg.N, dtype=torch.int32, device=dev)
+    mx = torch.empty(cfg.S, cfg.N, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, ddt.load().ddt_lm_head_argmax_workspace_size(cfg.S, cfg.B, cfg.V, d)),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        ddt.ddt_lm_head_argmax(Hd, Wd, nn, tok, mx, ws)
+    torch.cuda.synchronize()
+    ddt.lm_head_profiling(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(calls):
+        ddt.ddt_lm_head_argmax(Hd, Wd, nn, tok, mx, ws)
+    stop.record()
+    torch.cuda.synchronize()
+    tiles_ms, n = ddt.lm_head_timing()
+    ddt.lm_head_profiling(False)
+    call_s = start.elapsed_time(stop) / calls / 1e3
+    tiles_s = tiles_ms / max(n, 1) / 1e3
+    w = ddt.ddt_tree_walk_tokens(rnd.tree["tree_tok"], rnd.tree["parent"], nn, tok, cfg.L)
+    torch.cuda.synchronize()
+    same = all(torch.equal(w[k], rnd.walk[k]) for k in ("accept_len", "acc_nodes", "acc_tok", "bonus"))
+    M = cfg.S * cfg.N
+    flops = 2.0 * M * cfg.V * d
+    wbytes = cfg.V * d * 2 + M * d * 2 + M * 8
+    ridge = BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / wbytes >= ridge:
+        roof = {"bound": "mfma", "achieved": flops / tiles_s / 1e12, "peak": BF16_PEAK_TFS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": wbytes / tiles_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(cfg.name, "epilogue")
+    return {"kernel": "lm_head_tiles", "rows": M, "d_model": d, "vocab": cfg.V,
+            "kernel_us": tiles_s * 1e6, "call_us": call_s * 1e6, "launches_timed": n,
+            "roofline": roof, "flops_per_launch": flops, "bytes_per_launch": wbytes,
+            "logits_round_trip_avoided_bytes": 2 * M * cfg.V * 4,
+            "walk_matches_logits_walk": bool(same),
+            "timing": "HIP events attached to the tile kernel's dispatches; call_us adds the "
+                      "per-node reduce (torch events around the eager calls)"}
 
 
 def cpu_baseline(cfg, b, att, budget_s=12.0):
@@ -180,6 +242,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = auto)")
+    ap.add_argument("--no-epilogue", action="store_true", help="skip the fused LM-head epilogue")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -311,6 +374,10 @@ def main():
                                      "the two dispatches, same eager rounds"},
         "accept_len_mean": acc,
     }
+    if not args.no_epilogue and cfg.dtype == "bf16":
+        log("[bench] fused verifier epilogue")
+        del copies
+        out["epilogue"] = epilogue_bench(cfg, b, rnd, dev, up, workers)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(cfg, b, att)
