@@ -60,6 +60,7 @@ def load() -> ctypes.CDLL:
         "ddt_lm_head_argmax_workspace_size": (sz, [i32, i32, i64, i32]),
         "ddt_lm_head_argmax": (i32, [vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, sz, vp]),
         "ddt_tree_walk_tokens": (i32, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "ddt_tree_walk_strategy": (i32, [i32]),
         "ddt_lm_head_profiling": (i32, [i32]),
         "ddt_lm_head_timing": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
         "ddt_attention_profiling": (i32, [i32]),
@@ -79,7 +80,7 @@ EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_buil
            "ddt_adapt_budget", "ddt_tree_attention_workspace_size", "ddt_tree_attention",
            "ddt_commit_kv",
            "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_tree_walk_sample",
-           "ddt_tree_walk_noalloc_max_bytes",
+           "ddt_tree_walk_noalloc_max_bytes", "ddt_tree_walk_strategy",
            "ddt_tree_walk_noalloc", "ddt_lm_head_argmax_workspace_size", "ddt_lm_head_argmax",
            "ddt_tree_walk_tokens", "ddt_lm_head_profiling", "ddt_lm_head_timing",
            "ddt_attention_profiling", "ddt_attention_timing")
@@ -444,6 +445,18 @@ def ddt_tree_walk_tokens(tree_tok, parent, num_nodes, node_tok, L: int, out=None
                                     L, _p(out["accept_len"]), _p(out["acc_nodes"]), _p(out["acc_tok"]),
                                     _p(out["bonus"]), _stream(dev)), "ddt_tree_walk_tokens")
     return out
+
+
+WALK_AUTO, WALK_SCAN, WALK_PATH = 0, 1, 2
+
+
+def walk_strategy(mode: int) -> int:
+    """Set the tree walk's strategy for the process (WALK_AUTO, WALK_SCAN, WALK_PATH);
+    returns the previous one."""
+    prev = load().ddt_tree_walk_strategy(int(mode))
+    if prev < 0:
+        _check(prev, "ddt_tree_walk_strategy")
+    return prev
 
 
 def lm_head_profiling(enable: bool):

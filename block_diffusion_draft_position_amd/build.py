@@ -30,7 +30,9 @@ CFLAGS = [
 
 # per-file flags: the attention's max reductions need no NaN quieting (scores are
 # finite or -inf), so its kernels run with the IEEE mode bit off
-EXTRA = {"tree_attention.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+EXTRA = {"tree_attention.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+         # the path walk's maxima: the walk's scores are finite or -inf by its interface
+         "path_walk.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def sources():

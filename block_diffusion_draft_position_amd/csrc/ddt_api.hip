@@ -305,6 +305,11 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                                      as_stream(stream)));
 }
 
+int ddt_tree_walk_strategy(int mode) {
+  const int prev = set_walk_strategy(mode);
+  return prev < 0 ? DDT_ERR_INVALID_ARG : prev;
+}
+
 size_t ddt_lm_head_argmax_workspace_size(int S, int B, int64_t vocab, int d) {
   if (S < 1 || B < 0 || B > DDT_MAX_B || vocab < 1 || vocab > INT32_MAX - 512 || d < 64 ||
       d > 65536 || d % 64 != 0)

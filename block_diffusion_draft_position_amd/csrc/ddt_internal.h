@@ -17,6 +17,14 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
+// The sampling score fl(fl(x * t) + g) of the walk at temperature > 0: contraction into
+// a fused multiply-add would round once instead of twice and could change the arg-max,
+// so it is switched off here.
+__device__ __forceinline__ float sample_score(float x, float t, float g) {
+#pragma clang fp contract(off)
+  return x * t + g;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ unsigned long long ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
@@ -217,6 +225,19 @@ struct WalkPlan {
   size_t ws_bytes;       // counters + row counters + one 64-bit arg-max key per node
 };
 WalkPlan walk_plan(int S, int B, int64_t vocab);
+// true when the walk follows the path node by node (one workgroup per sequence,
+// scanning only the visited rows) rather than scanning every row
+bool path_walk_pays(int S, int B, int L, int64_t vocab);
+// the walk along the path: one workgroup per sequence, the visited rows only; no
+// workspace.  depth/gumbel/inv_t as launch_tree_walk (gumbel null: greedy).
+hipError_t launch_path_walk(const int32_t* tree_tok, const int32_t* parent,
+                            const int32_t* num_nodes, const float* target, int S, int B, int L,
+                            int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,
+                            int32_t* acc_tok, int32_t* bonus_out, hipStream_t st,
+                            const int32_t* depth, const float* gumbel, float inv_t);
+// 0: the planner decides; 1: always the row scan; 2: always the path walk.  Returns the
+// previous mode, or -1 for an invalid one.
+int set_walk_strategy(int mode);
 // The walk's static scratch (a file-scope device array of walk_scratch_bytes()): its
 // device address on the current device, looked up with hipGetSymbolAddress once per
 // device, whose first lookup also enqueues a zero fill on st.

@@ -2,7 +2,11 @@
 // the target's decoding rule from the root, accept while its token matches a child,
 // carry the first mismatch as the next bonus token).
 //
-// One kernel.  A workgroup takes one batch of one node's row of target logits (waves x
+// Two strategies with identical outputs.  The row scan below finds every node's arg-max
+// and then walks; the path walk (path_walk.hip) follows the walk and reads only the
+// rows of the nodes it visits.  The planner at the end of this file picks one per call.
+//
+// The row scan.  A workgroup takes one batch of one node's row of target logits (waves x
 // 64 lanes x 32 logits: 16 waves for a row that fits one batch, 8 otherwise, down to
 // 2 when the grid would leave CUs idle), loaded with 16-byte loads issued together,
 // and finds its arg-max: larger value first, equal values by smaller id.  Longer rows
@@ -24,6 +28,7 @@
 // 2080 rounds/s against 5950 (C1 -8%), so the ordering rests on the hardware's.
 #include <limits.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "ddt_internal.h"
@@ -55,13 +60,6 @@ __device__ __forceinline__ unsigned long long pack(float v, int id) {
 
 __device__ __forceinline__ int unpack_id(unsigned long long key) {
   return (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
-}
-
-// The sampling score fl(fl(x * t) + g): contraction into a fused multiply-add would
-// round once instead of twice and could change the arg-max, so it is switched off here.
-__device__ __forceinline__ float sample_score(float x, float t, float g) {
-#pragma clang fp contract(off)
-  return x * t + g;
 }
 
 // ONE: the whole grid runs at once, so the scan is on the latency path and takes the
@@ -285,6 +283,32 @@ hipError_t walk_scratch(void** ptr, hipStream_t st) {
   return hipSuccess;
 }
 
+// the caller's choice (ddt_tree_walk_strategy); 0 lets the planner decide
+static std::atomic<int> g_walk_strategy{0};
+
+int set_walk_strategy(int mode) {
+  if (mode < 0 || mode > 2) return -1;
+  return g_walk_strategy.exchange(mode);
+}
+
+// Which walk: the row scan reads all S * N rows at once (about 6 us plus the logits at
+// 6 TB/s); the path walk reads one row per accepted token plus one, in sequence, each
+// on one CU (about 2 us plus 1 us and a row at 90 GB/s per step): figures measured on
+// MI355X.  The path walk's time grows with the accepted length, which the planner does
+// not know in advance; it plans for half the block accepted (L / 2 tokens), a mid
+// value for the mean acceptance lengths the DDTree page reports (實驗結果與權衡:
+// about 11 of 16 at best), and takes the path walk when that beats the scan.  Of the
+// workloads, 32 sequences of 65 nodes over 128256 logits take it, and so do the tiny
+// rows of 64 logits, where both take a few microseconds.
+bool path_walk_pays(int S, int B, int L, int64_t vocab) {
+  const int mode = g_walk_strategy.load();
+  if (mode != 0) return mode == 2;
+  const double t_step = 1e-6 + (double)vocab * 4.0 / 9e10;
+  const double t_path = 2e-6 + (L / 2 + 1) * t_step;
+  const double t_scan = 6e-6 + (double)S * (B + 1) * (double)vocab * 4.0 / 6e12;
+  return t_path < t_scan;
+}
+
 WalkPlan walk_plan(int S, int B, int64_t vocab) {
   WalkPlan p;
   const int64_t rows = (int64_t)S * (B + 1);
@@ -320,6 +344,9 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
       static_cast<char*>(ws) + plan.counter_bytes + plan.rowcnt_bytes);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0) &&
                       (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0);
+  if (path_walk_pays(S, B, L, vocab))
+    return launch_path_walk(tree_tok, parent, num_nodes, target, S, B, L, vocab, accept_len,
+                            acc_nodes, acc_tok, bonus_out, st, depth, gumbel, inv_t);
   const dim3 grid((unsigned)((int64_t)S * N * plan.nbatch)), block(plan.waves * kWave);
   const size_t smem = 3 * sizeof(int) * N;
 #define DDT_WALK(ONE, SAMPLE)                                                                  \

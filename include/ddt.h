@@ -300,6 +300,24 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                   int32_t* accept_len, int32_t* acc_nodes, int32_t* acc_tok, int32_t* bonus_out,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* Strategy of ddt_tree_walk, ddt_tree_walk_sample and ddt_tree_walk_noalloc, for the
+ * whole process (both give identical outputs; the walk's result depends only on the
+ * rows of the nodes it visits):
+ *   DDT_WALK_AUTO (0)  the library chooses per call (the default);
+ *   DDT_WALK_SCAN (1)  arg-max of every node's row by many workgroups, then the walk;
+ *   DDT_WALK_PATH (2)  one workgroup per sequence follows the walk and scans only the
+ *                      rows of the nodes it visits (at most L + 1 rows, one after
+ *                      another), leaving the workspace untouched.
+ * AUTO takes PATH where even L + 1 sequential row scans are expected to beat the full
+ * scan (many long rows: S * (B + 1) rows of a large vocabulary).  Returns the previous
+ * strategy, or DDT_ERR_INVALID_ARG for a value outside 0..2 (the strategy is then
+ * unchanged).  Not synchronised with calls in flight on other threads.
+ */
+#define DDT_WALK_AUTO 0
+#define DDT_WALK_SCAN 1
+#define DDT_WALK_PATH 2
+int ddt_tree_walk_strategy(int mode);
+
 /* ---------------------------------------------------------------- step 5 at temperature > 0
  * Tree walk under the target's sampling rule at temperature T > 0 (中文摘要 counts
  * temperature among the evaluated settings; 運作流程 step 4 follows the target's

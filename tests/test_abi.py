@@ -225,3 +225,14 @@ def test_walk_tokens_validation():
     assert f(a[0], a[1], a[2], a[3], 0, 8, 4, a[4], a[5], a[6], a[7], None) == -1
     assert f(a[0], a[1], a[2], a[3], 1, 8, 0, a[4], a[5], a[6], a[7], None) == -1
     assert f(a[0], a[1], a[2], a[3], 1, 1024, 4, a[4], a[5], a[6], a[7], None) == -1
+
+
+def test_walk_strategy_setter():
+    f = ddt.load().ddt_tree_walk_strategy
+    assert f(3) == -1 and f(-1) == -1   # rejected; the strategy stays as it was
+    assert f(ddt.WALK_PATH) == ddt.WALK_AUTO
+    assert f(ddt.WALK_SCAN) == ddt.WALK_PATH
+    assert ddt.walk_strategy(ddt.WALK_AUTO) == ddt.WALK_SCAN
+    with pytest.raises(ddt.DDTError):
+        ddt.walk_strategy(7)
+    assert f(ddt.WALK_AUTO) == ddt.WALK_AUTO
