@@ -10,12 +10,23 @@
 //
 // lm_head_tiles<VT, MT, NWV, NWM>: one workgroup per VT x MT tile of the logits
 // (vocabulary x hidden rows), K = d in steps of 64.
+//   * Tile shape by the number of hidden rows M: 256 x 256 with eight waves (each 128
+//     vocabulary x 64 hidden rows, two waves per SIMD) above 128 rows; 256 x 128 with
+//     four waves above 64; narrower below.  Each K-step brings (VT + MT) rows of 128
+//     bytes into LDS for VT * MT * 128 flops: the 256 x 128 tile needs 48 bytes per
+//     clock per CU from L2 to keep the MFMAs busy, about what the L2 delivers, and the
+//     256 x 256 tile 32 (measured against the 256 x 128 tile: 32 x 65 rows 4.68 ->
+//     3.75 ms; 520 and 513 rows -13 to -14%; 129 rows -23%).
+//   * In the last row tile a wave's 32-row blocks with no live hidden row are neither
+//     read nor multiplied (a separate copy of the K loop, so that full tiles carry no
+//     test): with 2080 rows, the ninth 256-row tile holds 32.
 //   * W and H tiles go global -> LDS by buffer_load_dwordx4 ... lds (no registers in
-//     between) into a ring of NS stages (3 for the 256 x 128 tile: 144 KB, one
-//     workgroup per CU; 2 for the narrow tiles).  An LDS row is one tile row's 64
-//     K-values, 128 bytes in eight 16-byte slots; chunk c of row r sits in slot
-//     c ^ ((r >> 1) & 7), so that the 16 rows a 16-lane group reads in one fragment
-//     load fall in 16 distinct 16-byte bank groups (measured: no bank conflicts).
+//     between) into a ring of NS stages (2 for the 256 x 256 tile: 128 KB; 3 for the
+//     256 x 128 tile: 144 KB; one workgroup per CU; 2 for the narrow tiles).  An LDS
+//     row is one tile row's 64 K-values, 128 bytes in eight 16-byte slots; chunk c of
+//     row r sits in slot c ^ ((r >> 1) & 7), so that the 16 rows a 16-lane group reads
+//     in one fragment load fall in 16 distinct 16-byte bank groups (measured: no bank
+//     conflicts).
 //   * One barrier per K-step, placed before the step's last substep: by then each wave
 //     holds that substep's fragments in registers, so the stage can be refilled, and
 //     having waited for its own loads of the next step, the next step's first
@@ -156,7 +167,12 @@ lm_head_tiles(const bf16_t* __restrict__ H, const bf16_t* __restrict__ Wt, int M
   const int frag_base = l32 * kRowBytes;
   const int fsw = (l32 >> 1) & 7;
   bf16x8 fa[2][C::VB], fb[2][C::MB];
-  auto rd = [&]<int ST, int KS, int BUF>() {
+  // the wave's 32-row blocks of hidden rows that hold live rows (all MB but in the
+  // last row tile); a block with none is neither read nor multiplied
+  const int mlive = __builtin_amdgcn_readfirstlane(
+      min(C::MB, max(0, (mrows - wm * C::MW + 31) / 32)));
+  auto rd = [&]<int ST, int KS, int BUF, bool GUARD>() {
+    if (GUARD && mlive == 0) return;
     const unsigned char* As = smem + ST * C::STAGE + (wv * C::VW) * kRowBytes + frag_base;
     const unsigned char* Bs = smem + ST * C::STAGE + (VT + wm * C::MW) * kRowBytes + frag_base;
     const int slot = (((2 * KS + h2) ^ fsw) << 4);
@@ -165,14 +181,16 @@ lm_head_tiles(const bf16_t* __restrict__ H, const bf16_t* __restrict__ Wt, int M
       fa[BUF][vb] = *reinterpret_cast<const bf16x8*>(As + vb * 32 * kRowBytes + slot);
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
-      fb[BUF][mb] = *reinterpret_cast<const bf16x8*>(Bs + mb * 32 * kRowBytes + slot);
+      if (!GUARD || mb < mlive)
+        fb[BUF][mb] = *reinterpret_cast<const bf16x8*>(Bs + mb * 32 * kRowBytes + slot);
   };
-  auto mfmas = [&]<int BUF>() {
+  auto mfmas = [&]<int BUF, bool GUARD>() {
 #pragma unroll
     for (int vb = 0; vb < C::VB; ++vb)
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
-        acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUF][vb], fb[BUF][mb], acc[vb][mb], 0, 0, 0);
+        if (!GUARD || mb < mlive)
+          acc[vb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUF][vb], fb[BUF][mb], acc[vb][mb], 0, 0, 0);
   };
   // the reads of the next substep between this substep's MFMAs, one after each MFMA
   auto interleave = [&]() {
@@ -192,15 +210,15 @@ lm_head_tiles(const bf16_t* __restrict__ H, const bf16_t* __restrict__ Wt, int M
   // wave then holds what it needs of stage ST, which is refilled with step s + NS, and
   // step s + 1's rows are visible, so its first fragments are read while substep 3's
   // MFMAs run.
-  auto step = [&]<int ST>(int s) {
-    rd.template operator()<ST, 1, 1>();
-    mfmas.template operator()<0>();
+  auto step = [&]<int ST, bool GUARD>(int s) {
+    rd.template operator()<ST, 1, 1, GUARD>();
+    mfmas.template operator()<0, GUARD>();
     interleave();
-    rd.template operator()<ST, 2, 0>();
-    mfmas.template operator()<1>();
+    rd.template operator()<ST, 2, 0, GUARD>();
+    mfmas.template operator()<1, GUARD>();
     interleave();
-    rd.template operator()<ST, 3, 1>();
-    mfmas.template operator()<0>();
+    rd.template operator()<ST, 3, 1, GUARD>();
+    mfmas.template operator()<0, GUARD>();
     interleave();
     if (s + 1 < nk) {
       if (NS == 3 && s + 2 < nk)
@@ -209,9 +227,9 @@ lm_head_tiles(const bf16_t* __restrict__ H, const bf16_t* __restrict__ Wt, int M
         __builtin_amdgcn_s_waitcnt(0x0070);               // lgkmcnt(0), vmcnt(0)
       __builtin_amdgcn_s_barrier();
       if (s + NS < nk) issue.template operator()<ST>(s + NS);
-      rd.template operator()<(ST + 1) % NS, 0, 0>();
+      rd.template operator()<(ST + 1) % NS, 0, 0, GUARD>();
     }
-    mfmas.template operator()<1>();
+    mfmas.template operator()<1, GUARD>();
   };
 
   // prologue: the first NS steps in flight, then step 0's rows
@@ -223,12 +241,18 @@ lm_head_tiles(const bf16_t* __restrict__ H, const bf16_t* __restrict__ Wt, int M
   else if (later == 1) __builtin_amdgcn_s_waitcnt(kWaitOne);
   else __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * C::PER_WAVE) & 15) | (((2 * C::PER_WAVE) >> 4) << 14));
   __builtin_amdgcn_s_barrier();
-  rd.template operator()<0, 0, 0>();
-  for (int s = 0; s < nk; s += NS) {
-    step.template operator()<0>(s);
-    if (s + 1 < nk) step.template operator()<1 % NS>(s + 1);
-    if (NS == 3 && s + 2 < nk) step.template operator()<2 % NS>(s + 2);
-  }
+  auto kloop = [&]<bool GUARD>() {
+    rd.template operator()<0, 0, 0, GUARD>();
+    for (int s = 0; s < nk; s += NS) {
+      step.template operator()<0, GUARD>(s);
+      if (s + 1 < nk) step.template operator()<1 % NS, GUARD>(s + 1);
+      if (NS == 3 && s + 2 < nk) step.template operator()<2 % NS, GUARD>(s + 2);
+    }
+  };
+  if (mlive == C::MB)
+    kloop.template operator()<false>();
+  else
+    kloop.template operator()<true>();
 
   // ---- epilogue.  Lane l holds, for column block mb, hidden row wm*MW + mb*32 + l%32
   // against vocabulary rows wv*VW + vb*32 + 8(r/4) + 4 h2 + r%4: visited in increasing
@@ -362,7 +386,7 @@ LmPlan lm_head_plan(int S, int B, int64_t vocab, int d) {
   LmPlan p{};
   const int64_t M = (int64_t)S * (B + 1);
   p.vt = 256;
-  p.mt = M > 64 ? 128 : M > 32 ? 64 : 32;
+  p.mt = M > 128 ? 256 : M > 64 ? 128 : M > 32 ? 64 : 32;
   p.nvt = (int)ceil_div(vocab, p.vt);
   p.ws_bytes = align_up((size_t)M * p.nvt * sizeof(Partial), 256);
   (void)d;
@@ -380,6 +404,7 @@ hipError_t launch_lm_head(const void* hidden, const void* weight, const int32_t*
   if (!lm_prof_events(&ev0, &ev1)) ev0 = ev1 = nullptr;
   hipError_t e;
   switch (p.mt) {
+    case 256: e = launch_tiles<256, 256, 2, 4, 2>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
     case 128: e = launch_tiles<256, 128, 2, 2, 3>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
     case 64: e = launch_tiles<256, 64, 4, 1, 2>(hidden, weight, M, V, d, part, st, ev0, ev1); break;
     default: e = launch_tiles<256, 32, 4, 1, 2>(hidden, weight, M, V, d, part, st, ev0, ev1); break;

@@ -84,12 +84,19 @@ def _planted(cfg, W, S, N, r, frac_unplanted=0.15):
 SMALL = [
     dict(S=1, B=16, V=3001, d=320),     # 17 rows
     dict(S=2, B=20, V=1000, d=128),     # 42 rows
-    dict(S=3, B=22, V=3001, d=320),     # 69 rows
-    dict(S=4, B=63, V=5000, d=64),      # 256 rows, two row tiles
+    dict(S=3, B=22, V=3001, d=320),     # 69 rows: 256 x 128 tile, the second wave's rows ragged
+    dict(S=4, B=63, V=5000, d=64),      # 256 rows: one full 256 x 256 tile
     dict(S=1, B=0, V=1, d=64),          # one row, one vocabulary entry
     dict(S=2, B=5, V=255, d=64),        # below one vocabulary tile
-    dict(S=1, B=200, V=257, d=192),     # 201 rows; one entry in the second tile
+    dict(S=1, B=200, V=257, d=192),     # 201 rows (the last wave holds 9); one entry in the
+                                        # second vocabulary tile
     dict(S=2, B=100, V=4096, d=1024),   # exact tiles, 16 K-steps
+    # above 256 rows: several 256 x 256 row tiles (eight waves of 64 rows), the last ragged
+    dict(S=1, B=256, V=3001, d=320),    # 257 rows: the second row tile holds one
+    dict(S=3, B=100, V=1000, d=128),    # 303 rows: 47 in the last tile (two blocks of one wave)
+    dict(S=2, B=300, V=4099, d=192),    # 602 rows: 90 in the last tile (two waves, three blocks)
+    dict(S=4, B=127, V=513, d=256),     # 512 rows: two full row tiles; one entry in the third
+                                        # vocabulary tile
 ]
 
 
@@ -109,34 +116,37 @@ def test_small_shapes(shape):
     assert V == 1 or dec >= planted   # every planted row is decided
 
 
-def test_exact_ties_go_to_the_smaller_id():
+@pytest.mark.parametrize("N", [40, 300])
+def test_exact_ties_go_to_the_smaller_id(N):
     # copies of a row's planted weight row placed at other ids: in the same wave's
     # block, the other lane half (ids 4 apart), another wave, another vocabulary tile,
-    # and after the original; equal weight rows give equal fp32 sums
-    V, d, S, N = 1024, 128, 1, 40
+    # and after the original; equal weight rows give equal fp32 sums.  40 rows take the
+    # narrow tile (64 vocabulary entries per wave), 300 the 256 x 256 tile (128 per wave)
+    V, d, S = 1024, 128, 1
     cfg = configs.custom("lmt", V=V, B=N - 1, S=S)
     W = gen.lm_head_weight(cfg, d).copy()
     toks = np.full(N, -1, dtype=np.int64)
     expect = {}
-    # (planted id, copy id), all ids distinct.  With 40 rows the kernel's tile is 256
-    # entries wide, 64 per wave: 701 sits in 700's 32-entry block; 706 and 710 are in
-    # the two lane halves of one block; 590 is in another wave than 650; 20, 255 and
-    # 900 are in other vocabulary tiles; the copies 701, 900 and 1 come after the
-    # original.
+    # (planted id, copy id), all ids distinct.  The tile is 256 entries wide: 701 sits
+    # in 700's 32-entry block; 706 and 710 are in the two lane halves of one block; 590
+    # is in another wave than 650 at 64 entries per wave; 20, 255 and 900 are in other
+    # vocabulary tiles; the copies 701, 900 and 1 come after the original.
     cases = [(700, 701), (710, 706), (650, 590), (300, 20), (500, 900), (1023, 255),
              (812, 808), (100, 99), (880, 879), (0, 1)]
     used = set()
     for m, (t, c) in enumerate(cases):
         assert t not in used and c not in used
         used.update((t, c))
-    for m, (t, c) in enumerate(cases):
+    # with 300 rows the tied rows sit in the last, partly filled row tile (rows 260 on)
+    first = 0 if N <= 256 else 260
+    for k, (t, c) in enumerate(cases):
         W[c] = W[t]
-        toks[m] = t
-        expect[m] = min(t, c)
+        toks[first + k] = t
+        expect[first + k] = (k, min(t, c))
     H = gen.hidden_states(cfg, 0, W, toks)[None]
     tok, mx = _run(H, W)
-    for m in expect:
-        assert int(tok[0, m]) == expect[m], (m, cases[m], int(tok[0, m]))
+    for m, (k, want) in expect.items():
+        assert int(tok[0, m]) == want, (m, cases[k], int(tok[0, m]))
         assert mx[0, m] == mx[0, m]  # finite
     # the rest of the rows still satisfy the oracle
     Hf = gen.bf16_bits_to_f32(H[0])
