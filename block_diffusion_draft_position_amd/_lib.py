@@ -447,12 +447,12 @@ def ddt_tree_walk_tokens(tree_tok, parent, num_nodes, node_tok, L: int, out=None
     return out
 
 
-WALK_AUTO, WALK_SCAN, WALK_PATH = 0, 1, 2
+WALK_AUTO, WALK_SCAN, WALK_PATH, WALK_HYBRID = 0, 1, 2, 3
 
 
 def walk_strategy(mode: int) -> int:
-    """Set the tree walk's strategy for the process (WALK_AUTO, WALK_SCAN, WALK_PATH);
-    returns the previous one."""
+    """Set the tree walk's strategy for the process (WALK_AUTO, WALK_SCAN, WALK_PATH,
+    WALK_HYBRID); returns the previous one."""
     prev = load().ddt_tree_walk_strategy(int(mode))
     if prev < 0:
         _check(prev, "ddt_tree_walk_strategy")

@@ -222,21 +222,27 @@ struct WalkPlan {
   bool short_scan;       // the grid fits the CUs at once: latency-path scan
   size_t counter_bytes;  // per-sequence completion counters at the front of the workspace
   size_t rowcnt_bytes;   // then per-row counters of finished batches
-  size_t ws_bytes;       // counters + row counters + one 64-bit arg-max key per node
+  size_t key_bytes;      // then one 64-bit arg-max key per node
+  size_t state_bytes;    // then the hybrid walk's hand-off {node, accepted, count} per sequence
+  size_t ws_bytes;       // all of the above + one subtree mark byte per node
 };
 WalkPlan walk_plan(int S, int B, int64_t vocab);
-// true when the walk follows the path node by node (one workgroup per sequence,
-// scanning only the visited rows) rather than scanning every row
-bool path_walk_pays(int S, int B, int L, int64_t vocab);
-// the walk along the path: one workgroup per sequence, the visited rows only; no
-// workspace.  depth/gumbel/inv_t as launch_tree_walk (gumbel null: greedy).
+// The walk's strategy: the row scan alone, the path walk alone, or the hybrid (the path
+// walk for *steps accepted tokens, then the scan over the reached node's subtree).
+enum class WalkMode { kScan, kPath, kHybrid };
+WalkMode walk_mode(int S, int B, int L, int64_t vocab, int* steps);
+// the walk along the path: one workgroup per sequence, the visited rows only.
+// depth/gumbel/inv_t as launch_tree_walk (gumbel null: greedy).  max_steps < 0: walk to
+// the end; else hand over after max_steps accepted tokens through state [S][4] and the
+// subtree marks sub [S, N] (both zero on entry).
 hipError_t launch_path_walk(const int32_t* tree_tok, const int32_t* parent,
                             const int32_t* num_nodes, const float* target, int S, int B, int L,
                             int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,
                             int32_t* acc_tok, int32_t* bonus_out, hipStream_t st,
-                            const int32_t* depth, const float* gumbel, float inv_t);
-// 0: the planner decides; 1: always the row scan; 2: always the path walk.  Returns the
-// previous mode, or -1 for an invalid one.
+                            const int32_t* depth, const float* gumbel, float inv_t,
+                            int max_steps, unsigned* state, unsigned char* sub);
+// 0: the planner decides; 1: always the row scan; 2: always the path walk; 3: always
+// the hybrid.  Returns the previous mode, or -1 for an invalid one.
 int set_walk_strategy(int mode);
 // The walk's static scratch (a file-scope device array of walk_scratch_bytes()): its
 // device address on the current device, looked up with hipGetSymbolAddress once per

@@ -18,6 +18,13 @@
 // maximum, and the workgroup's reduction breaks equal values by the smaller id.  A
 // thread that saw only -inf keeps its first float4.  Scores are finite or -inf (the
 // interface excludes NaN), so the no-NaN build of this file changes no result.
+//
+// With a step budget (the hybrid walk), a sequence whose walk is still going after
+// max_steps accepted tokens hands over to the row scan: the kernel records the current
+// node, the tokens accepted so far and the size of the current node's subtree
+// (state[s] = {node, accepted, count}), and marks the subtree's nodes (sub[s, n] = 1;
+// a node's subtree is itself and every node whose parent chain reaches it).  The scan
+// then reads only those rows and continues the walk from that node.
 #include <limits.h>
 
 #include "ddt_internal.h"
@@ -116,13 +123,14 @@ __global__ void __launch_bounds__(kThreads)
 path_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ parent,
                  const int32_t* __restrict__ num_nodes, const float* __restrict__ target,
                  const int32_t* __restrict__ depth, const float* __restrict__ gumbel, float inv_t,
-                 int N, int L, int V, bool vec_ok, int32_t* __restrict__ accept_len,
+                 int N, int L, int V, bool vec_ok, int max_steps, unsigned* __restrict__ state,
+                 unsigned char* __restrict__ sub, int32_t* __restrict__ accept_len,
                  int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
                  int32_t* __restrict__ bonus_out) {
   extern __shared__ int psm[];  // tok[N], parent[N], depth[N]
   __shared__ float rv[kThreads / kWave];
   __shared__ int ri[kThreads / kWave];
-  __shared__ int want_s, child_s;
+  __shared__ int want_s, child_s, count_s;
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int nn = min(max(num_nodes[s], 1), N);
@@ -134,10 +142,36 @@ path_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
     pr[i] = parent[(int64_t)s * N + i];
     if (SAMPLE) dp[i] = depth[(int64_t)s * N + i];
   }
-  if (tid == 0) child_s = INT_MAX;
+  if (tid == 0) {
+    child_s = INT_MAX;
+    count_s = 0;
+  }
   __syncthreads();
   int cur = 0, a = 0;
   for (;;) {
+    if (a == max_steps) {
+      // hand over to the scan: mark cur's subtree.  Parents precede their children, so
+      // a member's chain falls from it to cur in at most L links; a chain that leaves
+      // that order or runs longer belongs to no valid tree and marks nothing
+      for (int n = cur + tid; n < nn; n += kThreads) {
+        int x = n;
+        for (int k = 0; k <= L && x > cur; ++k) {
+          const int p = pr[x];
+          x = (p >= 0 && p < x) ? p : -1;
+        }
+        if (x == cur) {
+          sub[(int64_t)s * N + n] = 1;
+          atomicAdd(&count_s, 1);
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        state[4 * s] = (unsigned)cur;
+        state[4 * s + 1] = (unsigned)a;
+        state[4 * s + 2] = (unsigned)count_s;
+      }
+      return;  // the scan writes this sequence's remaining outputs
+    }
     const float* row = target + ((int64_t)s * N + cur) * V;
     const float* g = SAMPLE ? gumbel + ((int64_t)s * (L + 1) + dp[cur]) * V : nullptr;
     const int want = row_argmax<SAMPLE>(row, g, inv_t, V, vec_ok, rv, ri, &want_s);
@@ -174,19 +208,20 @@ hipError_t launch_path_walk(const int32_t* tree_tok, const int32_t* parent,
                             const int32_t* num_nodes, const float* target, int S, int B, int L,
                             int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,
                             int32_t* acc_tok, int32_t* bonus_out, hipStream_t st,
-                            const int32_t* depth, const float* gumbel, float inv_t) {
+                            const int32_t* depth, const float* gumbel, float inv_t,
+                            int max_steps, unsigned* state, unsigned char* sub) {
   const int N = B + 1;
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0) &&
                       (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0);
   const size_t smem = 3 * sizeof(int) * N;
   if (gumbel)
     hipLaunchKernelGGL((path_walk_kernel<true>), dim3(S), dim3(kThreads), smem, st, tree_tok, parent,
-                       num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, vec_ok, accept_len,
-                       acc_nodes, acc_tok, bonus_out);
+                       num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, vec_ok, max_steps,
+                       state, sub, accept_len, acc_nodes, acc_tok, bonus_out);
   else
     hipLaunchKernelGGL((path_walk_kernel<false>), dim3(S), dim3(kThreads), smem, st, tree_tok, parent,
-                       num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, vec_ok, accept_len,
-                       acc_nodes, acc_tok, bonus_out);
+                       num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, vec_ok, max_steps,
+                       state, sub, accept_len, acc_nodes, acc_tok, bonus_out);
   return hipGetLastError();
 }
 

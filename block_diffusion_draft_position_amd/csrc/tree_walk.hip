@@ -78,6 +78,7 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
                  const int32_t* __restrict__ depth, const float* __restrict__ gumbel, float inv_t,
                  int N, int L, int vocab, int nseg, bool vec_ok, unsigned long long* __restrict__ best,
                  unsigned* __restrict__ counters, unsigned* __restrict__ rowcnt,
+                 unsigned* __restrict__ state, unsigned char* __restrict__ sub,
                  int32_t* __restrict__ accept_len,
                  int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
                  int32_t* __restrict__ bonus_out) {
@@ -89,6 +90,13 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   const int n = (int)(row % N);
   const int nn = num_nodes[s];
   if (n >= nn) return;
+  // after a hand-off from the path walk only the marked subtree's rows take part (a
+  // sequence the path walk finished has none), and the count is theirs
+  int count = nn;
+  if (state) {
+    if (!sub[row]) return;
+    count = (int)state[4 * s + 2];
+  }
   const int nw = blockDim.x / kWave;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -178,7 +186,7 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
     }
     if (row_done) {
       const unsigned prev = atomicAdd(&counters[s], 1u);
-      last = prev == (unsigned)nn - 1u;
+      last = prev == (unsigned)count - 1u;
     }
   }
   if (!__builtin_amdgcn_readfirstlane(last)) return;
@@ -215,12 +223,21 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
     }
   }
   if (lane == 0) __hip_atomic_store(&counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the walk resumes where the path walk handed over (nodes outside that subtree have
+  // no key, and the walk never reaches them); the marks and the state are cleared
+  int cur = 0;
+  int a = 0;
+  if (state) {
+    // readfirstlane waits for the loads, so they complete before the stores below
+    cur = __builtin_amdgcn_readfirstlane((int)state[4 * s]);
+    a = __builtin_amdgcn_readfirstlane((int)state[4 * s + 1]);
+    for (int i = lane; i < nn; i += kWave) sub[(int64_t)s * N + i] = 0;
+    if (lane < 3) state[4 * s + lane] = 0u;
+  }
   // the wave's LDS writes above before its reads below
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int cur = 0;
-  int a = 0;
   while (a < L) {
     const int wt = want[cur];
     int found = -1;
@@ -287,26 +304,41 @@ hipError_t walk_scratch(void** ptr, hipStream_t st) {
 static std::atomic<int> g_walk_strategy{0};
 
 int set_walk_strategy(int mode) {
-  if (mode < 0 || mode > 2) return -1;
+  if (mode < 0 || mode > 3) return -1;
   return g_walk_strategy.exchange(mode);
 }
 
-// Which walk: the row scan reads all S * N rows at once (about 6 us plus the logits at
-// 6 TB/s); the path walk reads one row per accepted token plus one, in sequence, each
-// on one CU (about 2 us plus 1 us and a row at 90 GB/s per step): figures measured on
-// MI355X.  The path walk's time grows with the accepted length, which the planner does
-// not know in advance; it plans for half the block accepted (L / 2 tokens), a mid
-// value for the mean acceptance lengths the DDTree page reports (實驗結果與權衡:
-// about 11 of 16 at best), and takes the path walk when that beats the scan.  Of the
-// workloads, 32 sequences of 65 nodes over 128256 logits take it, and so do the tiny
-// rows of 64 logits, where both take a few microseconds.
-bool path_walk_pays(int S, int B, int L, int64_t vocab) {
-  const int mode = g_walk_strategy.load();
-  if (mode != 0) return mode == 2;
+// Which walk.  The row scan reads all S * N rows at once: about 6 us plus the logits at
+// 6 TB/s.  The path walk reads one row per accepted token plus one, in sequence, each on
+// one CU: about 2 us plus, per step, 1 us and a row at 90 GB/s (figures measured on
+// MI355X).  Its time grows with the accepted length, which is not known in advance.
+//   * Path walk when it wins even with half the block accepted (L / 2 tokens, a middle
+//     value for the mean acceptance lengths the DDTree page reports, 實驗結果與權衡:
+//     about 11 of 16 at best): 32 sequences of 65 nodes over 128256 logits, where the
+//     scan reads 1 GB; also the tiny rows of 64 logits.
+//   * Row scan when the scan is short anyway (under 15 us: one sequence of up to 128
+//     nodes, or a 32000-entry vocabulary).
+//   * Otherwise the hybrid: the path walk for up to kHybridSteps accepted tokens, then
+//     the scan over the subtree of the node it reached.  A walk that ends early (the
+//     common case) costs a few path steps plus a scan launch whose workgroups find
+//     nothing to do; a long one costs those steps plus a scan of the remaining
+//     subtree, which is smaller than the tree.
+constexpr int kHybridSteps = 3;
+
+WalkMode walk_mode(int S, int B, int L, int64_t vocab, int* steps) {
+  *steps = kHybridSteps;
+  switch (g_walk_strategy.load()) {
+    case 1: return WalkMode::kScan;
+    case 2: return WalkMode::kPath;
+    case 3: return WalkMode::kHybrid;
+    default: break;
+  }
   const double t_step = 1e-6 + (double)vocab * 4.0 / 9e10;
   const double t_path = 2e-6 + (L / 2 + 1) * t_step;
   const double t_scan = 6e-6 + (double)S * (B + 1) * (double)vocab * 4.0 / 6e12;
-  return t_path < t_scan;
+  if (t_path < t_scan) return WalkMode::kPath;
+  if (t_scan < 15e-6) return WalkMode::kScan;
+  return WalkMode::kHybrid;
 }
 
 WalkPlan walk_plan(int S, int B, int64_t vocab) {
@@ -327,7 +359,9 @@ WalkPlan walk_plan(int S, int B, int64_t vocab) {
   p.short_scan = rows * p.nbatch <= cu_count();
   p.counter_bytes = align_up((size_t)S * sizeof(unsigned), 256);
   p.rowcnt_bytes = align_up((size_t)rows * sizeof(unsigned), 256);
-  p.ws_bytes = p.counter_bytes + p.rowcnt_bytes + align_up((size_t)rows * sizeof(unsigned long long), 256);
+  p.key_bytes = align_up((size_t)rows * sizeof(unsigned long long), 256);
+  p.state_bytes = align_up((size_t)S * 4 * sizeof(unsigned), 256);
+  p.ws_bytes = p.counter_bytes + p.rowcnt_bytes + p.key_bytes + p.state_bytes + align_up((size_t)rows, 256);
   return p;
 }
 
@@ -338,21 +372,36 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
                             hipStream_t st, const int32_t* depth, const float* gumbel,
                             float inv_t) {
   const int N = B + 1;
-  unsigned* counters = static_cast<unsigned*>(ws);
-  unsigned* rowcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + plan.counter_bytes);
-  unsigned long long* best = reinterpret_cast<unsigned long long*>(
-      static_cast<char*>(ws) + plan.counter_bytes + plan.rowcnt_bytes);
+  char* w = static_cast<char*>(ws);
+  unsigned* counters = reinterpret_cast<unsigned*>(w);
+  unsigned* rowcnt = reinterpret_cast<unsigned*>(w + plan.counter_bytes);
+  unsigned long long* best = reinterpret_cast<unsigned long long*>(w + plan.counter_bytes + plan.rowcnt_bytes);
+  unsigned* state = reinterpret_cast<unsigned*>(w + plan.counter_bytes + plan.rowcnt_bytes + plan.key_bytes);
+  unsigned char* sub = reinterpret_cast<unsigned char*>(state) + plan.state_bytes;
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0) &&
                       (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0);
-  if (path_walk_pays(S, B, L, vocab))
+  int steps = 0;
+  const WalkMode mode = walk_mode(S, B, L, vocab, &steps);
+  if (mode == WalkMode::kPath)
     return launch_path_walk(tree_tok, parent, num_nodes, target, S, B, L, vocab, accept_len,
-                            acc_nodes, acc_tok, bonus_out, st, depth, gumbel, inv_t);
+                            acc_nodes, acc_tok, bonus_out, st, depth, gumbel, inv_t, -1, nullptr,
+                            nullptr);
+  if (mode == WalkMode::kHybrid) {
+    const hipError_t e = launch_path_walk(tree_tok, parent, num_nodes, target, S, B, L, vocab,
+                                          accept_len, acc_nodes, acc_tok, bonus_out, st, depth,
+                                          gumbel, inv_t, steps, state, sub);
+    if (e != hipSuccess) return e;
+  } else {
+    state = nullptr;
+    sub = nullptr;
+  }
   const dim3 grid((unsigned)((int64_t)S * N * plan.nbatch)), block(plan.waves * kWave);
   const size_t smem = 3 * sizeof(int) * N;
 #define DDT_WALK(ONE, SAMPLE)                                                                  \
   hipLaunchKernelGGL((tree_walk_kernel<ONE, SAMPLE>), grid, block, smem, st, tree_tok, parent, \
                      num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, plan.nbatch,     \
-                     vec_ok, best, counters, rowcnt, accept_len, acc_nodes, acc_tok, bonus_out)
+                     vec_ok, best, counters, rowcnt, state, sub, accept_len, acc_nodes, acc_tok, \
+                     bonus_out)
   if (gumbel) {
     if (plan.short_scan)
       DDT_WALK(true, true);

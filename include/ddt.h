@@ -289,8 +289,8 @@ int ddt_commit_kv(void* k_cache, void* v_cache, const int64_t* cu_prefix, int64_
  * bonus_out  [S]     the target's token at the last accepted node.
  * ws        at least ddt_tree_walk_workspace_size(S, B, vocab) bytes of device memory,
  *           zero-filled before its first use; every call leaves it zero-filled again
- *           (completion counters and arg-max keys).  Calls that share a workspace
- *           must not overlap.
+ *           (completion counters, arg-max keys, the hybrid walk's hand-off state and
+ *           subtree marks).  Calls that share a workspace must not overlap.
  * Errors: null pointer; S < 1; L outside [1, DDT_MAX_L]; B outside [0, DDT_MAX_B];
  *         vocab < 1 or > INT32_MAX; ws too small.
  */
@@ -301,21 +301,26 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
                   void* ws, size_t ws_bytes, void* stream);
 
 /* Strategy of ddt_tree_walk, ddt_tree_walk_sample and ddt_tree_walk_noalloc, for the
- * whole process (both give identical outputs; the walk's result depends only on the
+ * whole process (all give identical outputs; the walk's result depends only on the
  * rows of the nodes it visits):
- *   DDT_WALK_AUTO (0)  the library chooses per call (the default);
- *   DDT_WALK_SCAN (1)  arg-max of every node's row by many workgroups, then the walk;
- *   DDT_WALK_PATH (2)  one workgroup per sequence follows the walk and scans only the
- *                      rows of the nodes it visits (at most L + 1 rows, one after
- *                      another), leaving the workspace untouched.
- * AUTO takes PATH where even L + 1 sequential row scans are expected to beat the full
- * scan (many long rows: S * (B + 1) rows of a large vocabulary).  Returns the previous
- * strategy, or DDT_ERR_INVALID_ARG for a value outside 0..2 (the strategy is then
- * unchanged).  Not synchronised with calls in flight on other threads.
+ *   DDT_WALK_AUTO   (0)  the library chooses per call (the default);
+ *   DDT_WALK_SCAN   (1)  arg-max of every node's row by many workgroups, then the walk;
+ *   DDT_WALK_PATH   (2)  one workgroup per sequence follows the walk and scans only the
+ *                        rows of the nodes it visits (at most L + 1 rows, one after
+ *                        another), leaving the workspace untouched;
+ *   DDT_WALK_HYBRID (3)  the path walk for up to 3 accepted tokens; a sequence whose
+ *                        walk goes on is handed to the scan, which reads only the rows
+ *                        of the reached node's subtree and finishes the walk.
+ * AUTO takes PATH where it is expected to beat the full scan with half the block
+ * accepted (many long rows: S * (B + 1) rows of a large vocabulary), SCAN where the
+ * full scan is short, and HYBRID in between.  Returns the previous strategy, or
+ * DDT_ERR_INVALID_ARG for a value outside 0..3 (the strategy is then unchanged).  Not
+ * synchronised with calls in flight on other threads.
  */
 #define DDT_WALK_AUTO 0
 #define DDT_WALK_SCAN 1
 #define DDT_WALK_PATH 2
+#define DDT_WALK_HYBRID 3
 int ddt_tree_walk_strategy(int mode);
 
 /* ---------------------------------------------------------------- step 5 at temperature > 0
@@ -349,9 +354,9 @@ int ddt_tree_walk_sample(const int32_t* tree_tok, const int32_t* parent, const i
  * hipMalloc.  Arguments, outputs and errors are those of ddt_tree_walk; the kernels
  * are the same.  Its workspace is a static device array of the library,
  * ddt_tree_walk_noalloc_max_bytes() = 1 MiB, of which a call needs
- * ddt_tree_walk_workspace_size(S, B, vocab) bytes (256-byte-rounded 4 bytes per
- * sequence, then 4 + 8 bytes per node row: S * (B + 1) rows up to about 87000).  A
- * larger problem returns DDT_ERR_TOO_LARGE before any launch.
+ * ddt_tree_walk_workspace_size(S, B, vocab) bytes (each part 256-byte-rounded: 4 and
+ * 16 bytes per sequence, 4 + 8 + 1 bytes per node row: S * (B + 1) rows up to about
+ * 80000).  A larger problem returns DDT_ERR_TOO_LARGE before any launch.
  * Each GPU the library runs on holds its own copy of the array until the process
  * ends.  The first call on a device looks up the array's address there and enqueues
  * a zero fill of it on `stream` ahead of the walk; every walk leaves the part it used

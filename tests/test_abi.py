@@ -229,9 +229,10 @@ def test_walk_tokens_validation():
 
 def test_walk_strategy_setter():
     f = ddt.load().ddt_tree_walk_strategy
-    assert f(3) == -1 and f(-1) == -1   # rejected; the strategy stays as it was
+    assert f(4) == -1 and f(-1) == -1   # rejected; the strategy stays as it was
     assert f(ddt.WALK_PATH) == ddt.WALK_AUTO
-    assert f(ddt.WALK_SCAN) == ddt.WALK_PATH
+    assert f(ddt.WALK_HYBRID) == ddt.WALK_PATH
+    assert f(ddt.WALK_SCAN) == ddt.WALK_HYBRID
     assert ddt.walk_strategy(ddt.WALK_AUTO) == ddt.WALK_SCAN
     with pytest.raises(ddt.DDTError):
         ddt.walk_strategy(7)

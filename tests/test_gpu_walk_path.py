@@ -1,11 +1,13 @@
-"""The tree walk's two strategies through the C ABI (ddt_tree_walk_strategy): the row
-scan (every node's arg-max by many workgroups, then the walk) and the path walk (one
-workgroup per sequence scans only the rows of the nodes it visits).  Each is forced in
-turn and compared with the oracle's walk, bit-exact on accept lengths, accepted nodes
-and tokens and bonus tokens: ragged and 4-aligned vocabularies, rows longer than one
-pass of the path walk's loads, the interface's largest trees, long accepted paths,
-exact ties, the sampling walk and the allocation-free entry point.  The planner's own
-choice is covered by every other walk test."""
+"""The tree walk's three strategies through the C ABI (ddt_tree_walk_strategy): the row
+scan (every node's arg-max by many workgroups, then the walk), the path walk (one
+workgroup per sequence scans only the rows of the nodes it visits) and the hybrid (the
+path walk for up to three accepted tokens, then the scan over the reached node's
+subtree).  Each is forced in turn and compared with the oracle's walk, bit-exact on
+accept lengths, accepted nodes and tokens and bonus tokens: ragged and 4-aligned
+vocabularies, rows longer than one pass of the path walk's loads, the interface's
+largest trees, long accepted paths (which the hybrid hands over), exact ties, the
+sampling walk and the allocation-free entry point.  The planner's own choice is
+covered by every other walk test."""
 import numpy as np
 import pytest
 import torch
@@ -19,7 +21,7 @@ from _gpu import dev_tensor, target_for
 
 pytestmark = pytest.mark.gpu
 
-STRATEGIES = {"scan": ddt.WALK_SCAN, "path": ddt.WALK_PATH}
+STRATEGIES = {"scan": ddt.WALK_SCAN, "path": ddt.WALK_PATH, "hybrid": ddt.WALK_HYBRID}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -168,16 +170,17 @@ def test_sampling_walk_strategies(strategy, name, inv_t):
 
 
 def test_path_walk_noalloc_and_workspace_untouched():
-    """The allocation-free entry point under the path walk: same outputs as the oracle,
-    and a scan walk after it (which relies on the array being zero) still agrees."""
+    """The allocation-free entry point under each strategy in turn, hybrid walks with
+    hand-overs (accepted paths of 4-6 tokens) among them: same outputs as the oracle
+    every time, so each call left the array zero for the next (the scan relies on it)."""
     cfg = configs.custom("walk-na", cfg_id=750, S=4, L=6, V=4096, K=4, B=40, chain_boost=5.0)
     b = _batch(cfg, True)
     trees = _trees(cfg, b)
     tl = target_for(cfg, b, trees)
     try:
-        ddt.walk_strategy(ddt.WALK_PATH)
-        _check(cfg, trees, tl, _greedy(cfg, trees, tl, noalloc=True), "path noalloc")
-        ddt.walk_strategy(ddt.WALK_SCAN)
-        _check(cfg, trees, tl, _greedy(cfg, trees, tl, noalloc=True), "scan noalloc after path")
+        for mode in (ddt.WALK_PATH, ddt.WALK_SCAN, ddt.WALK_HYBRID, ddt.WALK_HYBRID, ddt.WALK_SCAN):
+            ddt.walk_strategy(mode)
+            acc = _check(cfg, trees, tl, _greedy(cfg, trees, tl, noalloc=True), f"noalloc mode {mode}")
+        assert max(acc) > 3, acc   # the hybrid handed over
     finally:
         ddt.walk_strategy(ddt.WALK_AUTO)
