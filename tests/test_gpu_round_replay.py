@@ -147,20 +147,36 @@ def _check_oracle(cfg, b, trees, tl, got):
                              f"{cfg.name} seq {s}")
 
 
-def test_walk_workspace_reuse_across_shapes():
+@pytest.mark.parametrize("strategy", ["auto", "scan", "hybrid"])
+def test_walk_workspace_reuse_across_shapes(strategy):
     """ddt_tree_walk on one workspace, sized for the largest call, several calls in a
-    row with different S, B and V (one row batch and several), and a shortfall tree;
-    every call must match the oracle and leave the workspace zero-filled."""
+    row with different S, B and V (one row batch and several), a shortfall tree and a
+    confident draft whose walk the hybrid hands over to the scan; every call must match
+    the oracle and leave the workspace zero-filled, under the planner's choice and under
+    the two strategies that use the workspace."""
     shapes = [dict(S=2, L=5, V=70000, K=4, B=30), dict(S=1, L=3, V=900, K=2, B=50),
               dict(S=4, L=4, V=128256, K=8, B=64), dict(S=3, L=6, V=5000, K=5, B=20),
+              dict(S=3, L=8, V=4099, K=4, B=60, chain_boost=5.0),
               dict(S=2, L=5, V=70000, K=4, B=30)]
     need = max(ddt.load().ddt_tree_walk_workspace_size(sh["S"], sh["B"], sh["V"]) for sh in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    mode = {"auto": ddt.WALK_AUTO, "scan": ddt.WALK_SCAN, "hybrid": ddt.WALK_HYBRID}[strategy]
+    ddt.walk_strategy(mode)
+    try:
+        _reuse_calls(shapes, ws, strategy)
+    finally:
+        ddt.walk_strategy(ddt.WALK_AUTO)
+
+
+def _reuse_calls(shapes, ws, strategy):
     for i, sh in enumerate(shapes):
-        print(f"[case] walk call {i}: {sh}", flush=True)
+        print(f"[case] walk {strategy} call {i}: {sh}", flush=True)
         cfg = configs.custom(f"walk-reuse-{i}", cfg_id=300 + i, prefix=(1, 1), Hq=1, Hkv=1, D=32,
                              dtype="f32", **sh)
         b = gen.batch(cfg, with_qkv=False)
+        confident = "chain_boost" in sh
+        if confident:
+            b["keep"][:] = True
         trees = {}
         for s in range(cfg.S):
             tok, lq = oracle.topk(b["draft_logits"][s], cfg.K)
@@ -171,11 +187,15 @@ def test_walk_workspace_reuse_across_shapes():
         nn = dev_tensor(np.array([trees[s]["num_nodes"] for s in range(cfg.S)], dtype=np.int32))
         w = ddt.ddt_tree_walk(tt, par, nn, dev_tensor(tl), cfg.L, ws=ws)
         torch.cuda.synchronize()
+        acc = []
         for s in range(cfg.S):
             ref = oracle.tree_walk(trees[s]["tree_tok"], trees[s]["parent"], int(trees[s]["num_nodes"]),
                                    tl[s], cfg.L)
             for k in ("accept_len", "acc_nodes", "acc_tok", "bonus"):
                 assert np.array_equal(w[k][s].cpu().numpy(), ref[k]), f"call {i} seq {s}: {k}"
+            acc.append(int(ref["accept_len"]))
         assert not torch.any(ws), f"call {i}: workspace not left zero-filled"
+        if confident:
+            assert max(acc) > 3, acc   # a walk longer than the hybrid's three path steps
         if i == 1:
             assert int(trees[0]["num_nodes"]) < cfg.N, "call 1 must be a shortfall tree"
