@@ -184,3 +184,28 @@ def test_path_walk_noalloc_and_workspace_untouched():
         assert max(acc) > 3, acc   # the hybrid handed over
     finally:
         ddt.walk_strategy(ddt.WALK_AUTO)
+
+
+@pytest.mark.parametrize("inv_t", [1.0, 3.0])
+def test_sampling_walk_strategies_long_paths(strategy, inv_t):
+    """The sampling walk on confident drafts (accepted paths of several tokens, so the
+    hybrid hands its walks over to the scan with the noise rows of the later depths)."""
+    cfg = configs.custom("walk-sample-long", cfg_id=760, S=6, L=8, V=4099, K=4, B=60, chain_boost=5.0)
+    b = _batch(cfg, True)
+    trees = _trees(cfg, b)
+    tl = target_for(cfg, b, trees)
+    noise = np.stack([gen.gumbel_noise(cfg, s) for s in range(cfg.S)])
+    w = ddt.ddt_tree_walk_sample(_stack(cfg, trees, "tree_tok"), _stack(cfg, trees, "parent"),
+                                 _stack(cfg, trees, "depth"), _num_nodes(cfg, trees), dev_tensor(tl),
+                                 dev_tensor(noise), np.float32(inv_t), cfg.L)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in w.items()}
+    acc = []
+    for s in range(cfg.S):
+        t = trees[s]
+        ref = oracle.tree_walk_sample(t["tree_tok"], t["parent"], t["depth"], int(t["num_nodes"]),
+                                      tl[s], noise[s], np.float32(inv_t), cfg.L)
+        for k in ("accept_len", "acc_nodes", "acc_tok", "bonus"):
+            assert np.array_equal(got[k][s], ref[k]), f"{strategy} inv_t={inv_t} seq {s}: {k}"
+        acc.append(int(ref["accept_len"]))
+    assert max(acc) > 3, acc   # at least one walk goes past the hybrid's three path steps
