@@ -1042,7 +1042,11 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_
   p.rows_pad = p.row_groups * p.waves * 32;
   // prefix splits: about three (sequence, KV head, row group, split) units per CU
   // (measured best on C2, C3 B >= 256 and C4 against one, two and four), and no split
-  // above 16K keys so that unequal prefix lengths still spread evenly.  With few
+  // above 12K keys so that unequal prefix lengths still spread evenly.  The cap decides
+  // only when the units alone exceed three per CU (32 sequences of 16K-32K keys): there
+  // the splits are dealt to the resident workgroup slots in rounds, and 12K keys packed
+  // those rounds best (paired runs at that shape, main kernel plus merge: 4K +1%, 8K
+  // and 10K -1 to -2%, 12K -3.7%, 14K 0, 32K +8%, against 16K).  With few
   // (sequence, KV head, row group) units, up to a quarter of the CUs, three per CU cuts
   // each unit into many splits of two to four tiles, whose partials outweigh the keys
   // they cover; one per CU is then better (paired runs: C3 B = 16 to 128, +6-10%
@@ -1053,7 +1057,7 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_
   const int64_t maxp = std::max<int64_t>(max_prefix, 0);
   const int64_t want = std::max<int64_t>(1, ceil_div(target, units_base));
   int64_t chunk = (int64_t)align_up((size_t)std::max<int64_t>(1, ceil_div(maxp, want)), kTile);
-  chunk = std::min<int64_t>(std::max<int64_t>(chunk, kTile), 16384);
+  chunk = std::min<int64_t>(std::max<int64_t>(chunk, kTile), 12288);
   p.chunk = chunk;
   p.nsplit = (int)std::max<int64_t>(1, ceil_div(maxp, chunk));
   const size_t rows = (size_t)S * Hkv * (p.nsplit + 1) * p.rows_pad;
