@@ -2,9 +2,11 @@
 // the target's decoding rule from the root, accept while its token matches a child,
 // carry the first mismatch as the next bonus token).
 //
-// Two strategies with identical outputs.  The row scan below finds every node's arg-max
-// and then walks; the path walk (path_walk.hip) follows the walk and reads only the
-// rows of the nodes it visits.  The planner at the end of this file picks one per call.
+// Three strategies with identical outputs.  The row scan below finds every node's
+// arg-max and then walks; the path walk (path_walk.hip) follows the walk and reads only
+// the rows of the nodes it visits; the hybrid runs the path walk for a few steps and
+// hands a walk that goes on to the row scan, restricted to the reached node's subtree.
+// walk_mode (below) picks one per call.
 //
 // The row scan.  A workgroup takes one batch of one node's row of target logits (waves x
 // 64 lanes x 32 logits: 16 waves for a row that fits one batch, 8 otherwise, down to
