@@ -93,6 +93,9 @@ SHAPES = [
     ("deep-64", dict(S=2, L=64, V=40, K=2, B=150, chain_boost=200.0), True),
     ("widest", dict(S=1, L=3, V=5000, K=64, B=1023), False),
     ("wide-deep", dict(S=2, L=16, V=300, K=4, B=1023, chain_boost=200.0), True),
+    # every position accepted with L = 3: the hybrid hands over at a node of depth L,
+    # whose subtree is itself, and the scan only takes the bonus there
+    ("L3-full", dict(S=3, L=3, V=4096, K=4, B=40, chain_boost=200.0), True),
 ]
 
 
