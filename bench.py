@@ -365,7 +365,9 @@ def main():
                    "vocab": cfg.V, "top_k": cfg.K, "node_budget": cfg.B,
                    "prefix_tokens": int(np.sum(b["prefix_lens"])), "q_heads": cfg.Hq,
                    "kv_heads": cfg.Hkv, "head_dim": cfg.D, "rows_per_kv_head": R,
-                   "input_copies": ncopies, "graph_replay": not args.no_graph},
+                   "input_copies": ncopies, "graph_replay": not args.no_graph,
+                   "walk": {ddt.WALK_SCAN: "row scan", ddt.WALK_PATH: "path walk",
+                            ddt.WALK_HYBRID: "hybrid"}[ddt.walk_mode(cfg.S, cfg.B, cfg.L, cfg.V)]},
         "roofline": roof,
         "attention_step": {"kernels": [roof["kernel"], "attn_combine"] if cfg.dtype == "bf16" else [roof["kernel"]],
                            "us": step_s * 1e6, "achieved": step_ach, "unit": roof["unit"],

@@ -61,6 +61,7 @@ def load() -> ctypes.CDLL:
         "ddt_lm_head_argmax": (i32, [vp, vp, vp, i32, i32, i32, i64, vp, vp, vp, sz, vp]),
         "ddt_tree_walk_tokens": (i32, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "ddt_tree_walk_strategy": (i32, [i32]),
+        "ddt_tree_walk_mode": (i32, [i32, i32, i32, i64]),
         "ddt_lm_head_profiling": (i32, [i32]),
         "ddt_lm_head_timing": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
         "ddt_attention_profiling": (i32, [i32]),
@@ -80,7 +81,7 @@ EXPORTS = ("ddt_status_string", "ddt_topk_workspace_size", "ddt_topk", "ddt_buil
            "ddt_adapt_budget", "ddt_tree_attention_workspace_size", "ddt_tree_attention",
            "ddt_commit_kv",
            "ddt_tree_walk_workspace_size", "ddt_tree_walk", "ddt_tree_walk_sample",
-           "ddt_tree_walk_noalloc_max_bytes", "ddt_tree_walk_strategy",
+           "ddt_tree_walk_noalloc_max_bytes", "ddt_tree_walk_strategy", "ddt_tree_walk_mode",
            "ddt_tree_walk_noalloc", "ddt_lm_head_argmax_workspace_size", "ddt_lm_head_argmax",
            "ddt_tree_walk_tokens", "ddt_lm_head_profiling", "ddt_lm_head_timing",
            "ddt_attention_profiling", "ddt_attention_timing")
@@ -457,6 +458,15 @@ def walk_strategy(mode: int) -> int:
     if prev < 0:
         _check(prev, "ddt_tree_walk_strategy")
     return prev
+
+
+def walk_mode(S: int, B: int, L: int, vocab: int) -> int:
+    """The strategy a walk of this shape would use now (WALK_SCAN, WALK_PATH or
+    WALK_HYBRID)."""
+    m = load().ddt_tree_walk_mode(S, B, L, vocab)
+    if m < 0:
+        _check(m, "ddt_tree_walk_mode")
+    return m
 
 
 def lm_head_profiling(enable: bool):

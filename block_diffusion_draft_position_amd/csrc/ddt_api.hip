@@ -310,6 +310,17 @@ int ddt_tree_walk_strategy(int mode) {
   return prev < 0 ? DDT_ERR_INVALID_ARG : prev;
 }
 
+int ddt_tree_walk_mode(int S, int B, int L, int64_t vocab) {
+  if (S < 1 || L < 1 || L > DDT_MAX_L || B < 0 || B > DDT_MAX_B || vocab < 1 || vocab > INT32_MAX)
+    return DDT_ERR_INVALID_ARG;
+  int steps = 0;
+  switch (walk_mode(S, B, L, vocab, &steps)) {
+    case WalkMode::kScan: return DDT_WALK_SCAN;
+    case WalkMode::kPath: return DDT_WALK_PATH;
+    default: return DDT_WALK_HYBRID;
+  }
+}
+
 size_t ddt_lm_head_argmax_workspace_size(int S, int B, int64_t vocab, int d) {
   if (S < 1 || B < 0 || B > DDT_MAX_B || vocab < 1 || vocab > INT32_MAX - 512 || d < 64 ||
       d > 65536 || d % 64 != 0)

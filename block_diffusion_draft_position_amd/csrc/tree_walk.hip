@@ -318,8 +318,8 @@ int set_walk_strategy(int mode) {
 //     value for the mean acceptance lengths the DDTree page reports, 實驗結果與權衡:
 //     about 11 of 16 at best): 32 sequences of 65 nodes over 128256 logits, where the
 //     scan reads 1 GB; also the tiny rows of 64 logits.
-//   * Row scan when the scan is short anyway (under 15 us: one sequence of up to 128
-//     nodes, or a 32000-entry vocabulary).
+//   * Row scan when the scan is short anyway (under 15 us: one sequence of up to about
+//     100 nodes over 128256 logits, or a 32000-entry vocabulary).
 //   * Otherwise the hybrid: the path walk for up to kHybridSteps accepted tokens, then
 //     the scan over the subtree of the node it reached.  A walk that ends early (the
 //     common case) costs a few path steps plus a scan launch whose workgroups find

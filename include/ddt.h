@@ -323,6 +323,12 @@ int ddt_tree_walk(const int32_t* tree_tok, const int32_t* parent, const int32_t*
 #define DDT_WALK_HYBRID 3
 int ddt_tree_walk_strategy(int mode);
 
+/* The strategy (DDT_WALK_SCAN, DDT_WALK_PATH or DDT_WALK_HYBRID) that a walk call of
+ * this shape would use now: the forced one if ddt_tree_walk_strategy set one, else the
+ * planner's choice.  No device access.  Errors: the shape errors of ddt_tree_walk.
+ */
+int ddt_tree_walk_mode(int S, int B, int L, int64_t vocab);
+
 /* ---------------------------------------------------------------- step 5 at temperature > 0
  * Tree walk under the target's sampling rule at temperature T > 0 (中文摘要 counts
  * temperature among the evaluated settings; 運作流程 step 4 follows the target's

@@ -237,3 +237,24 @@ def test_walk_strategy_setter():
     with pytest.raises(ddt.DDTError):
         ddt.walk_strategy(7)
     assert f(ddt.WALK_AUTO) == ddt.WALK_AUTO
+
+
+def test_walk_planner_choices():
+    """The planner's documented choices on the workloads' shapes: the path walk for 32
+    sequences of 65 nodes over 128256 logits and for the tiny rows, the row scan where
+    the full scan is short, the hybrid in between; a forced strategy overrides it."""
+    from ddt_synthetic import configs
+    want = {"C0": ddt.WALK_PATH, "C1": ddt.WALK_SCAN, "C2": ddt.WALK_HYBRID, "C4": ddt.WALK_PATH,
+            "C3-B16": ddt.WALK_SCAN, "C3-B64": ddt.WALK_SCAN, "C3-B128": ddt.WALK_HYBRID,
+            "C3-B256": ddt.WALK_HYBRID,
+            "C3-B512": ddt.WALK_HYBRID}
+    for name, mode in want.items():
+        cfg = configs.get(name)
+        assert ddt.walk_mode(cfg.S, cfg.B, cfg.L, cfg.V) == mode, name
+    assert ddt.walk_strategy(ddt.WALK_SCAN) == ddt.WALK_AUTO
+    try:
+        assert ddt.walk_mode(32, 64, 16, 128256) == ddt.WALK_SCAN
+    finally:
+        ddt.walk_strategy(ddt.WALK_AUTO)
+    assert ddt.load().ddt_tree_walk_mode(0, 64, 16, 128256) == -1
+    assert ddt.load().ddt_tree_walk_mode(1, 64, 0, 128256) == -1
