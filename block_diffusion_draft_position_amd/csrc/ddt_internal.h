@@ -224,7 +224,7 @@ struct WalkPlan {
   size_t rowcnt_bytes;   // then per-row counters of finished batches
   size_t key_bytes;      // then one 64-bit arg-max key per node
   size_t state_bytes;    // then the hybrid walk's hand-off {node, accepted, count} per sequence
-  size_t ws_bytes;       // all of the above + one subtree mark byte per node
+  size_t ws_bytes;       // all of the above + the hand-off subtree's rows, one int per node
 };
 WalkPlan walk_plan(int S, int B, int64_t vocab);
 // The walk's strategy: the row scan alone, the path walk alone, or the hybrid (the path
@@ -234,13 +234,13 @@ WalkMode walk_mode(int S, int B, int L, int64_t vocab, int* steps);
 // the walk along the path: one workgroup per sequence, the visited rows only.
 // depth/gumbel/inv_t as launch_tree_walk (gumbel null: greedy).  max_steps < 0: walk to
 // the end; else hand over after max_steps accepted tokens through state [S][4] and the
-// subtree marks sub [S, N] (both zero on entry).
+// subtree's rows list [S, N] (both zero on entry).
 hipError_t launch_path_walk(const int32_t* tree_tok, const int32_t* parent,
                             const int32_t* num_nodes, const float* target, int S, int B, int L,
                             int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,
                             int32_t* acc_tok, int32_t* bonus_out, hipStream_t st,
                             const int32_t* depth, const float* gumbel, float inv_t,
-                            int max_steps, unsigned* state, unsigned char* sub);
+                            int max_steps, unsigned* state, int32_t* list);
 // 0: the planner decides; 1: always the row scan; 2: always the path walk; 3: always
 // the hybrid.  Returns the previous mode, or -1 for an invalid one.
 int set_walk_strategy(int mode);

@@ -20,11 +20,12 @@
 // interface excludes NaN), so the no-NaN build of this file changes no result.
 //
 // With a step budget (the hybrid walk), a sequence whose walk is still going after
-// max_steps accepted tokens hands over to the row scan: the kernel records the current
-// node, the tokens accepted so far and the size of the current node's subtree
-// (state[s] = {node, accepted, count}), and marks the subtree's nodes (sub[s, n] = 1;
-// a node's subtree is itself and every node whose parent chain reaches it).  The scan
-// then reads only those rows and continues the walk from that node.
+// max_steps accepted tokens hands over to the subtree scan: the kernel records the
+// current node, the tokens accepted so far and the size of the current node's subtree
+// (state[s] = {node, accepted, count}), and lists the subtree's nodes in
+// list[s, 0 .. count) in no particular order (a node's subtree is itself and every node
+// whose parent chain reaches it).  The scan then reads only those rows and continues
+// the walk from that node.
 #include <limits.h>
 
 #include "ddt_internal.h"
@@ -124,7 +125,7 @@ path_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
                  const int32_t* __restrict__ num_nodes, const float* __restrict__ target,
                  const int32_t* __restrict__ depth, const float* __restrict__ gumbel, float inv_t,
                  int N, int L, int V, bool vec_ok, int max_steps, unsigned* __restrict__ state,
-                 unsigned char* __restrict__ sub, int32_t* __restrict__ accept_len,
+                 int32_t* __restrict__ list, int32_t* __restrict__ accept_len,
                  int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
                  int32_t* __restrict__ bonus_out) {
   extern __shared__ int psm[];  // tok[N], parent[N], depth[N]
@@ -150,19 +151,16 @@ path_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   int cur = 0, a = 0;
   for (;;) {
     if (a == max_steps) {
-      // hand over to the scan: mark cur's subtree.  Parents precede their children, so
+      // hand over to the scan: list cur's subtree.  Parents precede their children, so
       // a member's chain falls from it to cur in at most L links; a chain that leaves
-      // that order or runs longer belongs to no valid tree and marks nothing
+      // that order or runs longer belongs to no valid tree and lists nothing
       for (int n = cur + tid; n < nn; n += kThreads) {
         int x = n;
         for (int k = 0; k <= L && x > cur; ++k) {
           const int p = pr[x];
           x = (p >= 0 && p < x) ? p : -1;
         }
-        if (x == cur) {
-          sub[(int64_t)s * N + n] = 1;
-          atomicAdd(&count_s, 1);
-        }
+        if (x == cur) list[(int64_t)s * N + atomicAdd(&count_s, 1)] = n;
       }
       __syncthreads();
       if (tid == 0) {
@@ -209,7 +207,7 @@ hipError_t launch_path_walk(const int32_t* tree_tok, const int32_t* parent,
                             int64_t vocab, int32_t* accept_len, int32_t* acc_nodes,
                             int32_t* acc_tok, int32_t* bonus_out, hipStream_t st,
                             const int32_t* depth, const float* gumbel, float inv_t,
-                            int max_steps, unsigned* state, unsigned char* sub) {
+                            int max_steps, unsigned* state, int32_t* list) {
   const int N = B + 1;
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0) &&
                       (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0);
@@ -217,11 +215,11 @@ hipError_t launch_path_walk(const int32_t* tree_tok, const int32_t* parent,
   if (gumbel)
     hipLaunchKernelGGL((path_walk_kernel<true>), dim3(S), dim3(kThreads), smem, st, tree_tok, parent,
                        num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, vec_ok, max_steps,
-                       state, sub, accept_len, acc_nodes, acc_tok, bonus_out);
+                       state, list, accept_len, acc_nodes, acc_tok, bonus_out);
   else
     hipLaunchKernelGGL((path_walk_kernel<false>), dim3(S), dim3(kThreads), smem, st, tree_tok, parent,
                        num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, vec_ok, max_steps,
-                       state, sub, accept_len, acc_nodes, acc_tok, bonus_out);
+                       state, list, accept_len, acc_nodes, acc_tok, bonus_out);
   return hipGetLastError();
 }
 

@@ -5,8 +5,8 @@
 // Three strategies with identical outputs.  The row scan below finds every node's
 // arg-max and then walks; the path walk (path_walk.hip) follows the walk and reads only
 // the rows of the nodes it visits; the hybrid runs the path walk for a few steps and
-// hands a walk that goes on to the row scan, restricted to the reached node's subtree.
-// walk_mode (below) picks one per call.
+// hands a walk that goes on to the subtree scan (below), which reads only the rows of
+// the reached node's subtree.  walk_mode (below) picks one per call.
 //
 // The row scan.  A workgroup takes one batch of one node's row of target logits (waves x
 // 64 lanes x 32 logits: 16 waves for a row that fits one batch, 8 otherwise, down to
@@ -64,6 +64,81 @@ __device__ __forceinline__ int unpack_id(unsigned long long key) {
   return (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
 }
 
+// The sequence's last workgroup (its wave 0): collect the target's token at every node
+// from the keys, clear keys and counter for the next call, and walk from node cur with
+// a tokens already accepted (the root and 0, or where the path walk handed over: nodes
+// outside that subtree have no key, and the walk never reaches them).
+__device__ __forceinline__ void finish_walk(int s, int N, int L, int nn, int cur, int a,
+                                            const int32_t* __restrict__ tree_tok,
+                                            const int32_t* __restrict__ parent,
+                                            unsigned long long* __restrict__ best,
+                                            unsigned* __restrict__ counters, int* smem,
+                                            int32_t* __restrict__ accept_len,
+                                            int32_t* __restrict__ acc_nodes,
+                                            int32_t* __restrict__ acc_tok,
+                                            int32_t* __restrict__ bonus_out) {
+  const int lane = threadIdx.x % kWave;
+  int* want = smem;         // [N] target's greedy token at each node
+  int* tok = smem + N;      // [N]
+  int* par = smem + 2 * N;  // [N]
+  // kGather nodes per lane have their loads in flight together: a load at a time made
+  // this gather a chain of round trips (C3, B = 512: 6 us for 513 nodes)
+  for (int i0 = 0; i0 < nn; i0 += kGather * kWave) {
+    unsigned long long k[kGather];
+    int t[kGather], p[kGather];
+#pragma unroll
+    for (int j = 0; j < kGather; ++j) {
+      const int i = i0 + j * kWave + lane;
+      if (i < nn) {
+        k[j] = __hip_atomic_load(best + (int64_t)s * N + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t[j] = tree_tok[(int64_t)s * N + i];
+        p[j] = parent[(int64_t)s * N + i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kGather; ++j) {
+      const int i = i0 + j * kWave + lane;
+      if (i < nn) {
+        // cleared for the next call, whose maxima start from 0
+        __hip_atomic_store(best + (int64_t)s * N + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        want[i] = unpack_id(k[j]);
+        tok[i] = t[j];
+        par[i] = p[j];
+      }
+    }
+  }
+  if (lane == 0) __hip_atomic_store(&counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the wave's LDS writes above before its reads below
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  while (a < L) {
+    const int wt = want[cur];
+    int found = -1;
+    for (int x0 = 0; x0 < nn && found < 0; x0 += kWave) {
+      const int xi = x0 + lane;
+      const bool hit = xi < nn && par[xi] == cur && tok[xi] == wt;
+      const unsigned long long m = ballot(hit);
+      if (m) found = x0 + __ffsll((long long)m) - 1;
+    }
+    if (found < 0) break;
+    if (lane == 0) {
+      acc_nodes[(int64_t)s * L + a] = found;
+      acc_tok[(int64_t)s * L + a] = tok[found];
+    }
+    cur = found;
+    ++a;
+  }
+  for (int i = a + lane; i < L; i += kWave) {
+    acc_nodes[(int64_t)s * L + i] = -1;
+    acc_tok[(int64_t)s * L + i] = -1;
+  }
+  if (lane == 0) {
+    accept_len[s] = a;
+    bonus_out[s] = want[cur];
+  }
+}
+
 // ONE: the whole grid runs at once, so the scan is on the latency path and takes the
 // batch maximum first (a short dependent chain); when workgroups stream in rounds, the
 // compare-as-you-go scan keeps up with the loads better (measured).  Two workgroups
@@ -80,7 +155,6 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
                  const int32_t* __restrict__ depth, const float* __restrict__ gumbel, float inv_t,
                  int N, int L, int vocab, int nseg, bool vec_ok, unsigned long long* __restrict__ best,
                  unsigned* __restrict__ counters, unsigned* __restrict__ rowcnt,
-                 unsigned* __restrict__ state, unsigned char* __restrict__ sub,
                  int32_t* __restrict__ accept_len,
                  int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
                  int32_t* __restrict__ bonus_out) {
@@ -92,13 +166,6 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   const int n = (int)(row % N);
   const int nn = num_nodes[s];
   if (n >= nn) return;
-  // after a hand-off from the path walk only the marked subtree's rows take part (a
-  // sequence the path walk finished has none), and the count is theirs
-  int count = nn;
-  if (state) {
-    if (!sub[row]) return;
-    count = (int)state[4 * s + 2];
-  }
   const int nw = blockDim.x / kWave;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -188,13 +255,15 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
     }
     if (row_done) {
       const unsigned prev = atomicAdd(&counters[s], 1u);
-      last = prev == (unsigned)count - 1u;
+      last = prev == (unsigned)nn - 1u;
     }
   }
   if (!__builtin_amdgcn_readfirstlane(last)) return;
 
   // the sequence's last workgroup (its wave 0): collect the target's token at every
-  // node, walk
+  // node, walk.  (finish_walk above is the same code, for the subtree scan; written out
+  // here because through that function the compiler kept a pointer live across the
+  // scan and spilled it in the maximum-first variant.)
   int* want = smem;         // [N] target's greedy token at each node
   int* tok = smem + N;      // [N]
   int* par = smem + 2 * N;  // [N]
@@ -225,21 +294,12 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
     }
   }
   if (lane == 0) __hip_atomic_store(&counters[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // the walk resumes where the path walk handed over (nodes outside that subtree have
-  // no key, and the walk never reaches them); the marks and the state are cleared
-  int cur = 0;
-  int a = 0;
-  if (state) {
-    // readfirstlane waits for the loads, so they complete before the stores below
-    cur = __builtin_amdgcn_readfirstlane((int)state[4 * s]);
-    a = __builtin_amdgcn_readfirstlane((int)state[4 * s + 1]);
-    for (int i = lane; i < nn; i += kWave) sub[(int64_t)s * N + i] = 0;
-    if (lane < 3) state[4 * s + lane] = 0u;
-  }
   // the wave's LDS writes above before its reads below
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int cur = 0;
+  int a = 0;
   while (a < L) {
     const int wt = want[cur];
     int found = -1;
@@ -264,6 +324,127 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
   if (lane == 0) {
     accept_len[s] = a;
     bonus_out[s] = want[cur];
+  }
+}
+
+// The hybrid's scan: the rows of the subtree the path walk handed over (state[s] =
+// {node, accepted, count}, the rows in list[s, 0 .. count)), a fixed grid of gs
+// workgroups per sequence looping over the (row, batch) items, so that a sequence the
+// path walk finished (count 0) costs its workgroups one load each.  An item is scanned
+// as in tree_walk_kernel (compare-as-you-go) and counted the same way; the two
+// reduction buffers alternate between items, so one barrier per item keeps a wave from
+// overwriting what wave 0 still reads.  The workgroup that completes the sequence has
+// no items left (its last item completed the count), clears the list and the state,
+// and walks on from the hand-off node.
+template <bool SAMPLE>
+__global__ void __launch_bounds__(kMaxWaves * kWave) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 4 : 8, 8)))
+subtree_scan_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict__ parent,
+                    const int32_t* __restrict__ num_nodes, const float* __restrict__ target,
+                    const int32_t* __restrict__ depth, const float* __restrict__ gumbel,
+                    float inv_t, int N, int L, int vocab, int nseg, int gs, bool vec_ok,
+                    unsigned long long* __restrict__ best, unsigned* __restrict__ counters,
+                    unsigned* __restrict__ rowcnt, unsigned* __restrict__ state,
+                    int32_t* __restrict__ list, int32_t* __restrict__ accept_len,
+                    int32_t* __restrict__ acc_nodes, int32_t* __restrict__ acc_tok,
+                    int32_t* __restrict__ bonus_out) {
+  __shared__ unsigned long long red[2][kMaxWaves];
+  extern __shared__ int smem[];
+  const int s = (int)(blockIdx.x / (unsigned)gs);
+  const int g = (int)(blockIdx.x % (unsigned)gs);
+  // the first item's list entry is read together with the state, not after it (g < gs
+  // <= N * nseg keeps it inside the sequence's list); each later one a step ahead
+  int next = list[(int64_t)s * N + g / nseg];
+  const int nn = min(max(num_nodes[s], 1), N);
+  // (clamped: a workspace that was not zero on entry gives wrong outputs, not stray reads)
+  const int count = __builtin_amdgcn_readfirstlane(min((int)state[4 * s + 2], nn));
+  const int items = count * nseg;
+  if (g >= items) return;  // also every workgroup of a sequence the path walk finished
+  const int nw = blockDim.x / kWave;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  int buf = 0;
+  for (int j = g; j < items; j += gs) {
+    const int seg = j % nseg;
+    const int n = __builtin_amdgcn_readfirstlane(min(max(next, 0), nn - 1));
+    if (j + gs < items) next = list[(int64_t)s * N + (j + gs) / nseg];
+    const int64_t row = (int64_t)s * N + n;
+    const float* x = target + row * (int64_t)vocab;
+    const float* gn = nullptr;
+    if constexpr (SAMPLE) gn = gumbel + ((int64_t)s * (L + 1) + depth[row]) * vocab;
+    // the batch's loads all issued before any compare: one memory latency per item
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    const int lo = (seg * nw + wave) * kWave * kE;
+    float v[kE];
+#pragma unroll
+    for (int b = 0; b < kE / 4; ++b) {
+      const int base = lo + (b * kWave + lane) * 4;
+      if (vec_ok && base + 3 < vocab) {
+        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + base));
+        if constexpr (SAMPLE) {
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(gn + base);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[4 * b + q] = sample_score(t[q], inv_t, gv[q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[4 * b + q] = t[q];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float e = -INFINITY;
+          if (base + q < vocab) {
+            e = x[base + q];
+            if constexpr (SAMPLE) e = sample_score(e, inv_t, gn[base + q]);
+          }
+          v[4 * b + q] = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int i = lo + ((e / 4) * kWave + lane) * 4 + e % 4;
+      if (i < vocab && better(v[e], i, bv, bi)) {
+        bv = v[e];
+        bi = i;
+      }
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) red[buf][wave] = bi == INT_MAX ? 0ull : pack(bv, bi);
+    __syncthreads();
+    if (wave == 0) {
+      bool last = false;
+      if (lane == 0) {
+        unsigned long long key = red[buf][0];
+        for (int w = 1; w < nw; ++w) key = red[buf][w] > key ? red[buf][w] : key;
+        // as in tree_walk_kernel: each atomic's result awaited before the next
+        const unsigned long long old = atomicMax(&best[row], key);
+        asm volatile("" ::"v"((unsigned)old) : "memory");
+        bool row_done = true;
+        if (nseg > 1) {
+          const unsigned pr = atomicAdd(&rowcnt[row], 1u);
+          asm volatile("" ::"v"(pr) : "memory");
+          row_done = pr == (unsigned)nseg - 1u;
+          if (row_done) __hip_atomic_store(&rowcnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (row_done) {
+          const unsigned prev = atomicAdd(&counters[s], 1u);
+          last = prev == (unsigned)count - 1u;
+        }
+      }
+      if (__builtin_amdgcn_readfirstlane(last)) {
+        // readfirstlane waits for the loads, so they complete before the stores below
+        const int cur = __builtin_amdgcn_readfirstlane((int)state[4 * s]);
+        const int a = __builtin_amdgcn_readfirstlane((int)state[4 * s + 1]);
+        for (int i = lane; i < count; i += kWave) list[(int64_t)s * N + i] = 0;
+        if (lane < 3) state[4 * s + lane] = 0u;
+        finish_walk(s, N, L, nn, cur, a, tree_tok, parent, best, counters, smem, accept_len,
+                    acc_nodes, acc_tok, bonus_out);
+        return;
+      }
+    }
+    buf ^= 1;
   }
 }
 
@@ -363,7 +544,8 @@ WalkPlan walk_plan(int S, int B, int64_t vocab) {
   p.rowcnt_bytes = align_up((size_t)rows * sizeof(unsigned), 256);
   p.key_bytes = align_up((size_t)rows * sizeof(unsigned long long), 256);
   p.state_bytes = align_up((size_t)S * 4 * sizeof(unsigned), 256);
-  p.ws_bytes = p.counter_bytes + p.rowcnt_bytes + p.key_bytes + p.state_bytes + align_up((size_t)rows, 256);
+  p.ws_bytes = p.counter_bytes + p.rowcnt_bytes + p.key_bytes + p.state_bytes +
+               align_up((size_t)rows * sizeof(int32_t), 256);
   return p;
 }
 
@@ -379,7 +561,7 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
   unsigned* rowcnt = reinterpret_cast<unsigned*>(w + plan.counter_bytes);
   unsigned long long* best = reinterpret_cast<unsigned long long*>(w + plan.counter_bytes + plan.rowcnt_bytes);
   unsigned* state = reinterpret_cast<unsigned*>(w + plan.counter_bytes + plan.rowcnt_bytes + plan.key_bytes);
-  unsigned char* sub = reinterpret_cast<unsigned char*>(state) + plan.state_bytes;
+  int32_t* list = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(state) + plan.state_bytes);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(target) % 16 == 0) && (vocab % 4 == 0) &&
                       (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0);
   int steps = 0;
@@ -388,22 +570,33 @@ hipError_t launch_tree_walk(const int32_t* tree_tok, const int32_t* parent,
     return launch_path_walk(tree_tok, parent, num_nodes, target, S, B, L, vocab, accept_len,
                             acc_nodes, acc_tok, bonus_out, st, depth, gumbel, inv_t, -1, nullptr,
                             nullptr);
+  const size_t smem = 3 * sizeof(int) * N;
   if (mode == WalkMode::kHybrid) {
     const hipError_t e = launch_path_walk(tree_tok, parent, num_nodes, target, S, B, L, vocab,
                                           accept_len, acc_nodes, acc_tok, bonus_out, st, depth,
-                                          gumbel, inv_t, steps, state, sub);
+                                          gumbel, inv_t, steps, state, list);
     if (e != hipSuccess) return e;
-  } else {
-    state = nullptr;
-    sub = nullptr;
+    // about two workgroups per CU over all sequences, at most one per item
+    const int gs = (int)std::max<int64_t>(
+        1, std::min<int64_t>((int64_t)N * plan.nbatch, ceil_div(2 * (int64_t)cu_count(), S)));
+    const dim3 sgrid((unsigned)((int64_t)S * gs)), sblock(plan.waves * kWave);
+    if (gumbel)
+      hipLaunchKernelGGL((subtree_scan_kernel<true>), sgrid, sblock, smem, st, tree_tok, parent,
+                         num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, plan.nbatch, gs,
+                         vec_ok, best, counters, rowcnt, state, list, accept_len, acc_nodes, acc_tok,
+                         bonus_out);
+    else
+      hipLaunchKernelGGL((subtree_scan_kernel<false>), sgrid, sblock, smem, st, tree_tok, parent,
+                         num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, plan.nbatch, gs,
+                         vec_ok, best, counters, rowcnt, state, list, accept_len, acc_nodes, acc_tok,
+                         bonus_out);
+    return hipGetLastError();
   }
   const dim3 grid((unsigned)((int64_t)S * N * plan.nbatch)), block(plan.waves * kWave);
-  const size_t smem = 3 * sizeof(int) * N;
 #define DDT_WALK(ONE, SAMPLE)                                                                  \
   hipLaunchKernelGGL((tree_walk_kernel<ONE, SAMPLE>), grid, block, smem, st, tree_tok, parent, \
                      num_nodes, target, depth, gumbel, inv_t, N, L, (int)vocab, plan.nbatch,     \
-                     vec_ok, best, counters, rowcnt, state, sub, accept_len, acc_nodes, acc_tok, \
-                     bonus_out)
+                     vec_ok, best, counters, rowcnt, accept_len, acc_nodes, acc_tok, bonus_out)
   if (gumbel) {
     if (plan.short_scan)
       DDT_WALK(true, true);

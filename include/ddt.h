@@ -290,7 +290,7 @@ int ddt_commit_kv(void* k_cache, void* v_cache, const int64_t* cu_prefix, int64_
  * ws        at least ddt_tree_walk_workspace_size(S, B, vocab) bytes of device memory,
  *           zero-filled before its first use; every call leaves it zero-filled again
  *           (completion counters, arg-max keys, the hybrid walk's hand-off state and
- *           subtree marks).  Calls that share a workspace must not overlap.
+ *           subtree rows).  Calls that share a workspace must not overlap.
  * Errors: null pointer; S < 1; L outside [1, DDT_MAX_L]; B outside [0, DDT_MAX_B];
  *         vocab < 1 or > INT32_MAX; ws too small.
  */
@@ -361,8 +361,8 @@ int ddt_tree_walk_sample(const int32_t* tree_tok, const int32_t* parent, const i
  * are the same.  Its workspace is a static device array of the library,
  * ddt_tree_walk_noalloc_max_bytes() = 1 MiB, of which a call needs
  * ddt_tree_walk_workspace_size(S, B, vocab) bytes (each part 256-byte-rounded: 4 and
- * 16 bytes per sequence, 4 + 8 + 1 bytes per node row: S * (B + 1) rows up to about
- * 80000).  A larger problem returns DDT_ERR_TOO_LARGE before any launch.
+ * 16 bytes per sequence, 4 + 8 + 4 bytes per node row: S * (B + 1) rows up to about
+ * 65000).  A larger problem returns DDT_ERR_TOO_LARGE before any launch.
  * Each GPU the library runs on holds its own copy of the array until the process
  * ends.  The first call on a device looks up the array's address there and enqueues
  * a zero fill of it on `stream` ahead of the walk; every walk leaves the part it used
