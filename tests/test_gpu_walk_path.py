@@ -96,6 +96,9 @@ SHAPES = [
     # every position accepted with L = 3: the hybrid hands over at a node of depth L,
     # whose subtree is itself, and the scan only takes the bonus there
     ("L3-full", dict(S=3, L=3, V=4096, K=4, B=40, chain_boost=200.0), True),
+    # a shortfall tree (31 nodes for a budget of 50: rows past num_nodes are padding)
+    # whose walk of 4 tokens the hybrid hands over
+    ("shortfall-deep", dict(S=2, L=4, V=600, K=2, B=50, chain_boost=200.0), True),
 ]
 
 
