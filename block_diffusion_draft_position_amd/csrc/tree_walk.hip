@@ -435,8 +435,8 @@ subtree_scan_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restr
       }
       if (__builtin_amdgcn_readfirstlane(last)) {
         // readfirstlane waits for the loads, so they complete before the stores below
-        const int cur = __builtin_amdgcn_readfirstlane((int)state[4 * s]);
-        const int a = __builtin_amdgcn_readfirstlane((int)state[4 * s + 1]);
+        const int cur = __builtin_amdgcn_readfirstlane(min(max((int)state[4 * s], 0), nn - 1));
+        const int a = __builtin_amdgcn_readfirstlane(min(max((int)state[4 * s + 1], 0), L));
         for (int i = lane; i < count; i += kWave) list[(int64_t)s * N + i] = 0;
         if (lane < 3) state[4 * s + lane] = 0u;
         finish_walk(s, N, L, nn, cur, a, tree_tok, parent, best, counters, smem, accept_len,
