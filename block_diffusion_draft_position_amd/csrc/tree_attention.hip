@@ -126,6 +126,18 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int64_t P = kc ? pre.length(u.s) : 0;
   const int64_t kstride = (int64_t)Hkv * D;   // elements between consecutive keys
   const bool tree = u.c == nsplit;
+  // A remainder group (the last row group of a unit) whose rows fit in one wave: the
+  // barrier-paced ring would keep one tile in flight for a single wave's work.  There
+  // waves 0 and 1 instead stream alternate tiles alone, each through one ring stage
+  // with no barrier, both for the same rows, and merge their two partials at the end;
+  // a wave whose rows fit in 16 computes one query block.  Prefix splits only.
+  const int grp_rows = R - u.rg * NW * 32;
+  const bool solo = NW >= 2 && !tree && grp_rows <= 32;
+  const bool one_qb = grp_rows <= 16;
+  const int wslot = solo ? 0 : wave;
+  // otherwise a wave whose 32 rows all lie past R (the last row group of a unit holds
+  // only the remainder) issues its share of the tile loads and meets the barriers, no more
+  const bool live = solo ? wave < 2 : (u.rg * NW + wave) * 32 < R;
   int64_t lo, hi;
   const bf16_t* kb;
   const bf16_t* vb;
@@ -403,7 +415,6 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
           int64_t chunk, int units, int row_groups, float scale_log2,
           float* __restrict__ opart, float2* __restrict__ mlpart) {
   constexpr int D = 128;
-  constexpr int NLOAD = (32 + NW - 1) / NW;  // 1 KB load instructions per wave per tile
 
   Unit u;
   if (!decode_block(Hkv, nsplit + 1, row_groups, units, u)) return;
@@ -412,9 +423,6 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int lane = tid % 64;
   const int g4 = lane / 16;   // 16-lane group
   const int l16 = lane % 16;
-  // a wave whose 32 rows all lie past R (the last row group of a unit holds only the
-  // remainder) issues its share of the tile loads and meets the barriers, no more
-  const bool live = (u.rg * NW + wave) * 32 < R;
 
   // per-sequence bounds, uniform across the workgroup: kept in scalar registers so that
   // the tile loop's bounds, tail tests and branches are scalar
@@ -423,6 +431,18 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int64_t P = kc ? rfl64(pre.length(u.s)) : 0;
   const int64_t kstride = (int64_t)Hkv * D;
   const bool tree = u.c == nsplit;
+  // A remainder group (the last row group of a unit) whose rows fit in one wave: the
+  // barrier-paced ring would keep one tile in flight for a single wave's work.  There
+  // waves 0 and 1 instead stream alternate tiles alone, each through one ring stage
+  // with no barrier, both for the same rows, and merge their two partials at the end;
+  // a wave whose rows fit in 16 computes one query block.  Prefix splits only.
+  const int grp_rows = R - u.rg * NW * 32;
+  const bool solo = NW >= 2 && !tree && grp_rows <= 32;
+  const bool one_qb = grp_rows <= 16;
+  const int wslot = solo ? 0 : wave;
+  // otherwise a wave whose 32 rows all lie past R (the last row group of a unit holds
+  // only the remainder) issues its share of the tile loads and meets the barriers, no more
+  const bool live = solo ? wave < 2 : (u.rg * NW + wave) * 32 < R;
   int64_t lo, hi;
   const bf16_t* kb;
   const bf16_t* vb;
@@ -460,7 +480,10 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const unsigned char* vbu = (const unsigned char*)rfl64((int64_t)vb);
   const uint32_t rowb = (uint32_t)kstride * 2;  // bytes per key row, a multiple of 256
   const uint32_t lane_base = (uint32_t)g4 * rowb + (uint32_t)((l16 ^ (2 * g4)) * 16);
-  auto issue = [&]<int ST>(int t_) {
+  // NI waves share a tile's loads (NI = NW), or wave 0 or 1 alone (NI = 1) issues all 32
+  auto issue = [&]<int ST, int NI = NW>(int t_) {
+    constexpr int NL = (32 + NI - 1) / NI;
+    const int wi = NI == 1 ? 0 : wave;
     const int t = __builtin_amdgcn_readfirstlane(t_);
     const int64_t t0 = (int64_t)t * kTile;  // from lo
     const int64_t tb = t0 * rowb;
@@ -468,13 +491,17 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbu + tb), (short)0, -1, kRsrcWord3);
     if (t0 + kTile <= span) {
 #pragma unroll
-      for (int j = 0; j < NLOAD; ++j) {
-        const int i = (wave + j * NW) & 31;
+      for (int j = 0; j < NL; ++j) {
+        const int i = (wi + j * NI) & 31;
         const bool isv = i >= 16;
         unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + (i & 15) * 1024;
         const uint32_t x = 16u * (8u * (i & 1) + ((i >> 1) & 1));
+        // (a lone issuing wave's row offsets are otherwise left in vector registers, and
+        // every load is wrapped in a loop over their distinct values)
+        uint32_t so = (uint32_t)(4 * (i & 15)) * rowb;
+        if constexpr (NI == 1) so = __builtin_amdgcn_readfirstlane(so);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_void*)dst, 16, lane_base ^ x,
-                                                 (uint32_t)(4 * (i & 15)) * rowb, 0, 0);
+                                                 so, 0, 0);
       }
     } else {
       // the split's last, partial tile: rows past the split re-read its last row.  (The
@@ -486,8 +513,8 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       asm volatile("" : "+v"(gl), "+v"(lchunk));
       const int last = (int)(span - 1 - t0);
 #pragma unroll
-      for (int j = 0; j < NLOAD; ++j) {
-        const int i = (wave + j * NW) & 31;
+      for (int j = 0; j < NL; ++j) {
+        const int i = (wi + j * NI) & 31;
         const bool isv = i >= 16;
         const int key = min(4 * (i & 15) + gl, last);
         const uint32_t off = (uint32_t)key * rowb + (lchunk ^ (16u * (8u * (i & 1) + ((i >> 1) & 1))));
@@ -503,7 +530,7 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   bf16x8 qf[2][4];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    rowq[qb] = (u.rg * NW + wave) * 32 + qb * 16 + l16;
+    rowq[qb] = (u.rg * NW + wslot) * 32 + qb * 16 + l16;
     nodeq[qb] = rowq[qb] / G;
     okq[qb] = rowq[qb] < R && nodeq[qb] < nn;
     const int head = u.g * G + (rowq[qb] % G);
@@ -541,29 +568,8 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
   for (int j = 0; j < 8; ++j) ones[j] = (bf16_t)1.f;
 
-  // ---- one tile from ring stage ST
-  auto step = [&]<int ST>(int t) {
-    // wait for this wave's loads of tile t: the only loads in flight (expcnt and
-    // lgkmcnt left at their maxima), then an execution barrier only: every wave has
-    // waited for its own loads, and the stage refilled next was read one barrier ago
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __builtin_amdgcn_s_barrier();
-    // the tree split's mask words for this tile, issued ahead of the next tile's loads so
-    // that waiting for them leaves those in flight.  The tile's 64 keys span words wi and
-    // wi + 1; wi < W always (the tile starts below nn <= N), and when wi + 1 == W the
-    // second word's keys all lie past N, masked by the tail test, so it re-reads word wi.
-    uint32_t w[2][2];
-    if (tree) {
-      const uint32_t wi = (uint32_t)t * (kTile / 32);
-      const uint32_t wj = min(wi + 1, (uint32_t)W - 1);
-      w[0][0] = *(const uint32_t*)(mseq + (mrow0 + wi * 4));
-      w[0][1] = *(const uint32_t*)(mseq + (mrow0 + wj * 4));
-      w[1][0] = *(const uint32_t*)(mseq + (mrow1 + wi * 4));
-      w[1][1] = *(const uint32_t*)(mseq + (mrow1 + wj * 4));
-    }
-    if (t + 1 < ntiles) issue.template operator()<ST ^ 1>(t + 1);
-    if (!live) return;
-
+  // ---- the math of tile t from ring stage ST, for QB query blocks of 16 rows
+  auto math = [&]<int ST, int QB>(int t, const uint32_t (&w)[2][2]) {
     // Per-lane offsets are re-materialised in every step (an empty asm hides their
     // loop invariance); otherwise the compiler keeps one copy per ring stage live.
     int kof[4];
@@ -596,26 +602,26 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
           sacc[qb][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][kb4], qf[qb][kk],
                                                                   kk == 0 ? f32x4{} : sacc[qb][kb4], 0, 0, 0);
     }
-    // order: the first two steps' reads, then per step two MFMAs per read of the next
+    // order: the first two steps' reads, then per step QB MFMAs per read of the next
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
       }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: bounded register use
     // ---- masks: ragged tail, and in the tree split the ancestor bits
     if (tree) {
       // bit (kin) of the two 32-key words; this lane's keys are kb4*16 + 4*g4 + r
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4) {
           const uint32_t bits = w[qb][kb4 >> 1] >> ((kb4 & 1) * 16 + g4 * 4);
@@ -630,15 +636,15 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (kb4 * 16 + g4 * 4 + r >= rem) {
-            sacc[0][kb4][r] = -INFINITY;
-            sacc[1][kb4][r] = -INFINITY;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[qb][kb4][r] = -INFINITY;
           }
     }
     // ---- online softmax (base 2), lazy rescale
-    bool need[2];
+    bool need[2] = {false, false};
     float tmax[2], m_use[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4)
@@ -653,7 +659,7 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       // tile as selects (74 multiplies per tile)
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         const float m_new = need[qb] ? tmax[qb] : m_run[qb];
         const float alpha = m_run[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         m_run[qb] = m_new;
@@ -663,10 +669,10 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       }
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+    for (int qb = 0; qb < QB; ++qb) m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
     bf16x8 pb[2][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
@@ -696,7 +702,7 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     // sum_k P[k][q] for every query: the same contraction with V replaced by ones
     // (the sum is of the bf16 weights the numerator uses); these cover the first reads
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
         lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][kh], lacc[qb], 0, 0, 0);
@@ -711,31 +717,109 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
+          for (int qb = 0; qb < QB; ++qb)
             oacc[qb][2 * pr + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[pr & 1][j][kh], pb[qb][kh],
                                                                             oacc[qb][2 * pr + j], 0, 0, 0);
     }
-    // order: the first pair's reads, the row sums, then per pair one MFMA per read of
-    // the next pair
+    // order: the first pair's reads, the row sums, then per pair QB MFMAs per two
+    // reads of the next pair (one and one for two blocks)
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 1);
 #pragma unroll
     for (int pr = 0; pr < 3; ++pr)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      for (int i = 0; i < 8 / (3 - QB); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3 - QB, 1);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 1);
   };
 
-  // prologue: tile 0 in flight.  Tile t uses stage t % 2; the loop is unrolled by the
-  // ring depth so every stage is a distinct object at compile time.
-  if (0 < ntiles) issue.template operator()<0>(0);
-  if (0 < ntiles) step.template operator()<0>(0);
-  for (int t = 1; t < ntiles; t += kStages) {
-    step.template operator()<1>(t);
-    if (t + 1 < ntiles) step.template operator()<0>(t + 1);
+  // ---- one tile from ring stage ST
+  auto step = [&]<int ST>(int t) {
+    // wait for this wave's loads of tile t: the only loads in flight (expcnt and
+    // lgkmcnt left at their maxima), then an execution barrier only: every wave has
+    // waited for its own loads, and the stage refilled next was read one barrier ago
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __builtin_amdgcn_s_barrier();
+    // the tree split's mask words for this tile, issued ahead of the next tile's loads so
+    // that waiting for them leaves those in flight.  The tile's 64 keys span words wi and
+    // wi + 1; wi < W always (the tile starts below nn <= N), and when wi + 1 == W the
+    // second word's keys all lie past N, masked by the tail test, so it re-reads word wi.
+    uint32_t w[2][2];
+    if (tree) {
+      const uint32_t wi = (uint32_t)t * (kTile / 32);
+      const uint32_t wj = min(wi + 1, (uint32_t)W - 1);
+      w[0][0] = *(const uint32_t*)(mseq + (mrow0 + wi * 4));
+      w[0][1] = *(const uint32_t*)(mseq + (mrow0 + wj * 4));
+      w[1][0] = *(const uint32_t*)(mseq + (mrow1 + wi * 4));
+      w[1][1] = *(const uint32_t*)(mseq + (mrow1 + wj * 4));
+    }
+    if (t + 1 < ntiles) issue.template operator()<ST ^ 1>(t + 1);
+    if (live) math.template operator()<ST, 2>(t, w);
+  };
+
+  if (!solo) {
+    // prologue: tile 0 in flight.  Tile t uses stage t % 2; the loop is unrolled by the
+    // ring depth so every stage is a distinct object at compile time.
+    if (0 < ntiles) issue.template operator()<0>(0);
+    if (0 < ntiles) step.template operator()<0>(0);
+    for (int t = 1; t < ntiles; t += kStages) {
+      step.template operator()<1>(t);
+      if (t + 1 < ntiles) step.template operator()<0>(t + 1);
+    }
+  } else {
+    // Wave ST (0 or 1) takes tiles ST, ST + 2, ... through stage ST: it waits for its
+    // own loads only, and refills the stage once its reads of it have returned.
+    const uint32_t wz[2][2] = {{0u, 0u}, {0u, 0u}};
+    auto stream = [&]<int ST, int QB>() {
+      if (ST < ntiles) issue.template operator()<ST, 1>(ST);
+      for (int t = ST; t < ntiles; t += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile t is in the stage
+        math.template operator()<ST, QB>(t, wz);
+        if (t + 2 < ntiles) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): every read of the stage returned
+          issue.template operator()<ST, 1>(t + 2);
+        }
+      }
+    };
+    if (wave == 0) {
+      if (one_qb) stream.template operator()<0, 1>();
+      else stream.template operator()<0, 2>();
+    } else if (wave == 1) {
+      if (one_qb) stream.template operator()<1, 1>();
+      else stream.template operator()<1, 2>();
+    }
+    // wave 1 hands its (O, max, sum) to wave 0 through the ring, now idle: O as
+    // [qb][db][lane] f32x4 in the K stages, (max, sum) as [qb][lane] in a V stage
+    f32x4* xo = reinterpret_cast<f32x4*>(g_ring_k0);
+    f32x2* xml = reinterpret_cast<f32x2*>(g_ring_v0);
+    __syncthreads();
+    if (wave == 1) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (qb == 1 && one_qb) break;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) xo[(qb * 8 + db) * 64 + lane] = oacc[qb][db];
+        xml[qb * 64 + lane] = f32x2{m_run[qb], lacc[qb][0]};
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (qb == 1 && one_qb) break;
+      const f32x2 o1 = xml[qb * 64 + lane];
+      const float m0 = m_run[qb], m1 = o1[0];
+      const float mm = fmaxf(m0, m1);
+      // a stream that saw no tile holds max -inf, sum 0 and O = 0
+      const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+      m_run[qb] = mm;
+      lacc[qb][0] = a0 * lacc[qb][0] + a1 * o1[1];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[qb][db] = a0 * oacc[qb][db] + a1 * xo[(qb * 8 + db) * 64 + lane];
+    }
   }
 
   // ---- partial results of this split

@@ -218,6 +218,23 @@ def test_narrow_attention_groups():
     run_case(cfg, rows_per_seq=240)
 
 
+@pytest.mark.parametrize("name,kw", [
+    # 152 rows per KV head: a full 128-row group and 24 rows left, so each of the two
+    # streams of the remainder group computes both 16-row query blocks
+    ("rem24", dict(S=4, B=18, prefix=(1500, 3000), Hq=16, Hkv=2)),
+    # 4 rows left and prefixes cut into one-tile splits: the second stream gets no tile
+    ("rem4-one-tile", dict(S=6, B=64, prefix=(5, 500), Hq=16, Hkv=4)),
+    # 8 rows left, three tiles per split (two for one stream, one for the other) and a
+    # ragged last tile in each sequence's last split
+    ("rem8-odd", dict(S=3, B=16, prefix=(2000, 4100), Hq=16, Hkv=2)),
+])
+def test_remainder_group_streams(name, kw):
+    """Remainder row groups of at most 32 rows: two waves stream alternate key tiles for
+    the same rows and merge their partial softmax states; every row is checked."""
+    cfg = configs.custom(name, L=4, V=500, K=4, D=128, dtype="bf16", **kw)
+    run_case(cfg)
+
+
 def test_signed_zero_ties():
     """-0.0 and +0.0 compare equal, so a tie between them goes to the smaller token id,
     in the top-K and in the walk's arg-max, as in the oracle."""
