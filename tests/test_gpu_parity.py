@@ -227,6 +227,9 @@ def test_narrow_attention_groups():
     # 8 rows left, three tiles per split (two for one stream, one for the other) and a
     # ragged last tile in each sequence's last split
     ("rem8-odd", dict(S=3, B=16, prefix=(2000, 4100), Hq=16, Hkv=2)),
+    # 1028 rows per KV head: eight full groups and 4 rows, the remainder groups dispatched
+    # after every full group
+    ("rem4-last", dict(S=2, B=256, prefix=(300, 700), Hq=32, Hkv=8)),
 ])
 def test_remainder_group_streams(name, kw):
     """Remainder row groups of at most 32 rows: two waves stream alternate key tiles for
