@@ -242,23 +242,30 @@ tree_walk_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restrict
     unsigned long long k = red[0];
     for (int w = 1; w < nw; ++w) k = red[w] > k ? red[w] : k;
     // the row's key is the maximum over its segments; the counters count finished
-    // segments per row and finished rows per sequence.  Each atomic's result is
-    // awaited before the next one is issued, which orders them without a fence.
-    const unsigned long long old = atomicMax(&best[row], k);
-    asm volatile("" ::"v"((unsigned)old) : "memory");  // the maximum has been performed
+    // segments per row and finished rows per sequence.  Each increment is a release at
+    // agent scope, publishing this workgroup's maximum; the workgroup that finishes a
+    // row takes an acquire fence before passing the row on, and the sequence's last
+    // one another before it reads best[], so it sees every maximum.  (Acquire-release
+    // increments in every workgroup made C1's round 8.6% longer than relaxed ones, this
+    // form 6%: each acquire invalidates the XCD's L2 under the other workgroups' logit
+    // reads, and each release writes it back.)
+    atomicMax(&best[row], k);
     bool row_done = true;
     if (nseg > 1) {
-      const unsigned pr = atomicAdd(&rowcnt[row], 1u);
-      asm volatile("" ::"v"(pr) : "memory");
+      const unsigned pr = __hip_atomic_fetch_add(&rowcnt[row], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       row_done = pr == (unsigned)nseg - 1u;
-      if (row_done) __hip_atomic_store(&rowcnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (row_done) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(&rowcnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     if (row_done) {
-      const unsigned prev = atomicAdd(&counters[s], 1u);
+      const unsigned prev = __hip_atomic_fetch_add(&counters[s], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       last = prev == (unsigned)nn - 1u;
     }
   }
   if (!__builtin_amdgcn_readfirstlane(last)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every row's maximum, before best[] is read
 
   // the sequence's last workgroup (its wave 0): collect the target's token at every
   // node, walk.  (finish_walk above is the same code, for the subtree scan; written out
@@ -418,22 +425,24 @@ subtree_scan_kernel(const int32_t* __restrict__ tree_tok, const int32_t* __restr
       if (lane == 0) {
         unsigned long long key = red[buf][0];
         for (int w = 1; w < nw; ++w) key = red[buf][w] > key ? red[buf][w] : key;
-        // as in tree_walk_kernel: each atomic's result awaited before the next
-        const unsigned long long old = atomicMax(&best[row], key);
-        asm volatile("" ::"v"((unsigned)old) : "memory");
+        // as in tree_walk_kernel: release increments, acquire fences where read
+        atomicMax(&best[row], key);
         bool row_done = true;
         if (nseg > 1) {
-          const unsigned pr = atomicAdd(&rowcnt[row], 1u);
-          asm volatile("" ::"v"(pr) : "memory");
+          const unsigned pr = __hip_atomic_fetch_add(&rowcnt[row], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
           row_done = pr == (unsigned)nseg - 1u;
-          if (row_done) __hip_atomic_store(&rowcnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (row_done) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(&rowcnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
         if (row_done) {
-          const unsigned prev = atomicAdd(&counters[s], 1u);
+          const unsigned prev = __hip_atomic_fetch_add(&counters[s], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
           last = prev == (unsigned)count - 1u;
         }
       }
       if (__builtin_amdgcn_readfirstlane(last)) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every row's maximum
         // readfirstlane waits for the loads, so they complete before the stores below
         const int cur = __builtin_amdgcn_readfirstlane(min(max((int)state[4 * s], 0), nn - 1));
         const int a = __builtin_amdgcn_readfirstlane(min(max((int)state[4 * s + 1], 0), L));
