@@ -452,6 +452,7 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   if (!decode_block_rl(Hkv, nsplit + 1, row_groups, units, rem_last, u)) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: kept in an SGPR
+  __builtin_assume(wave < NW);
   const int lane = tid % 64;
   const int g4 = lane / 16;   // 16-lane group
   const int l16 = lane % 16;
@@ -522,18 +523,34 @@ attn_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbu + tb), (short)0, -1, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbu + tb), (short)0, -1, kRsrcWord3);
     if (t0 + kTile <= span) {
+      if constexpr (16 % NI == 0) {
+        // NI divides 16: load j is wave wi's row block rb = wi + NI (j mod 16 / NI), of K
+        // for j < 16 / NI and of V after, so the operand is known at compile time and
+        // the row offset, destination and swizzle are the wave's own plus constants
+        // (recomputed from the wave index per tile they took ~100 scalar instructions
+        // and spilled scalar registers)
+        constexpr int PER = 16 / NI;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const int i = (wi + j * NI) & 31;
-        const bool isv = i >= 16;
-        unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + (i & 15) * 1024;
-        const uint32_t x = 16u * (8u * (i & 1) + ((i >> 1) & 1));
-        // (a lone issuing wave's row offsets are otherwise left in vector registers, and
-        // every load is wrapped in a loop over their distinct values)
-        uint32_t so = (uint32_t)(4 * (i & 15)) * rowb;
-        if constexpr (NI == 1) so = __builtin_amdgcn_readfirstlane(so);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_void*)dst, 16, lane_base ^ x,
-                                                 so, 0, 0);
+        for (int j = 0; j < NL; ++j) {
+          const bool isv = j >= PER;
+          const int rb = wi + NI * (j % PER);
+          unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + rb * 1024;
+          const uint32_t x = 16u * (8u * (rb & 1) + ((rb >> 1) & 1));
+          uint32_t so = (uint32_t)(4 * rb) * rowb;
+          if constexpr (NI == 1) so = __builtin_amdgcn_readfirstlane(so);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_void*)dst, 16, lane_base ^ x,
+                                                   so, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const int i = (wi + j * NI) & 31;
+          const bool isv = i >= 16;
+          unsigned char* dst = (isv ? ring_v<ST>() : ring_k<ST>()) + (i & 15) * 1024;
+          const uint32_t x = 16u * (8u * (i & 1) + ((i >> 1) & 1));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_void*)dst, 16, lane_base ^ x,
+                                                   (uint32_t)(4 * (i & 15)) * rowb, 0, 0);
+        }
       }
     } else {
       // the split's last, partial tile: rows past the split re-read its last row.  (The
