@@ -156,18 +156,6 @@ attn_partial_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int64_t P = kc ? pre.length(u.s) : 0;
   const int64_t kstride = (int64_t)Hkv * D;   // elements between consecutive keys
   const bool tree = u.c == nsplit;
-  // A remainder group (the last row group of a unit) whose rows fit in one wave: the
-  // barrier-paced ring would keep one tile in flight for a single wave's work.  There
-  // waves 0 and 1 instead stream alternate tiles alone, each through one ring stage
-  // with no barrier, both for the same rows, and merge their two partials at the end;
-  // a wave whose rows fit in 16 computes one query block.  Prefix splits only.
-  const int grp_rows = R - u.rg * NW * 32;
-  const bool solo = NW >= 2 && !tree && grp_rows <= 32;
-  const bool one_qb = grp_rows <= 16;
-  const int wslot = solo ? 0 : wave;
-  // otherwise a wave whose 32 rows all lie past R (the last row group of a unit holds
-  // only the remainder) issues its share of the tile loads and meets the barriers, no more
-  const bool live = solo ? wave < 2 : (u.rg * NW + wave) * 32 < R;
   int64_t lo, hi;
   const bf16_t* kb;
   const bf16_t* vb;
