@@ -1,7 +1,9 @@
 """Tree attention through one reused workspace and replayed from a HIP graph (as the
 benchmark runs it): every call and every replay must give the first eager call's
-bits, and that call must match the oracle.  The shapes are grids small enough to sit
-on the GPU at once (the latency-bound plan: wide row groups, one-tile splits)."""
+bits, and that call must match the oracle.  Two shapes are grids small enough to sit
+on the GPU at once (the latency-bound plan: wide row groups, one-tile splits); two take
+the narrow plan, whose last row group of each (sequence, KV head) holds 4 rows and runs
+as two streams, dispatched among the full groups or after all of them."""
 import math
 
 import numpy as np
@@ -22,6 +24,10 @@ pytestmark = pytest.mark.gpu
 SHAPES = {
     "two-row-groups": dict(S=1, L=8, V=1000, K=4, B=63, prefix=(768, 768), Hq=16, Hkv=2),
     "ragged": dict(S=3, L=5, V=800, K=4, B=30, prefix=(0, 700), Hq=8, Hkv=2),
+    # (3) 260 rows per KV head in groups of 128: two full groups and 4 rows
+    "remainder-streams": dict(S=6, L=4, V=500, K=4, B=64, prefix=(900, 3000), Hq=16, Hkv=4),
+    # (4) 1028 rows per KV head: eight full groups, the 4-row groups dispatched last
+    "remainder-last": dict(S=2, L=4, V=500, K=4, B=256, prefix=(300, 700), Hq=32, Hkv=8),
 }
 
 
