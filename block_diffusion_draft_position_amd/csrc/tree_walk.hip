@@ -539,12 +539,14 @@ WalkPlan walk_plan(int S, int B, int64_t vocab) {
   // A row that fits one batch of 16 waves is one workgroup; longer rows are split into
   // batches of 8 waves (8 * 64 * kE logits), one workgroup each, so no row makes a lone
   // extra round of the grid (8-wave batches measured 5-6% faster than 16 on C2 and C3).
-  // A grid of fewer workgroups than CUs splits its rows further, down to 2-wave
-  // batches, so that more CUs stream the logits (C1: 33 rows become 264 workgroups;
-  // 1% more rounds/s than 4-wave batches and 2.5% more than 16, paired runs).
+  // A grid of fewer workgroups than CUs splits a 16-wave row into 8-wave batches, and
+  // no further: every batch publishes its maximum with an agent-scope release (an L2
+  // writeback), so a few wide batches beat many narrow ones that reach more CUs
+  // (paired runs against splitting down to 2-wave batches: C1, 33 rows in 66 instead
+  // of 264 workgroups, 46.8 -> 45.5 us per round; C3 B = 16 63.5 -> 61.4 us).
   const int64_t per_wave = (int64_t)kWave * kE;
   int w = vocab <= kMaxWaves * per_wave ? kMaxWaves : kMaxWaves / 2;
-  while (w > 2 && rows * ceil_div(vocab, (int64_t)w * per_wave) < cu_count()) w /= 2;
+  while (w > 8 && rows * ceil_div(vocab, (int64_t)w * per_wave) < cu_count()) w /= 2;
   p.waves = (int)std::min<int64_t>(w, ceil_div(vocab, per_wave));
   p.nbatch = (int)ceil_div(vocab, (int64_t)p.waves * per_wave);
   // the whole grid at once on the CUs: the scan is on the latency path
