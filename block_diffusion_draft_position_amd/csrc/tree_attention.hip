@@ -1171,9 +1171,12 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int dtype, int64_t max_
   // (sequence, KV head, row group) units, up to a quarter of the CUs, three per CU cuts
   // each unit into many splits of two to four tiles, whose partials outweigh the keys
   // they cover; one per CU is then better (paired runs: C3 B = 16 to 128, +6-10%
-  // rounds/s).
+  // rounds/s).  Since the short remainder groups stream on their own, units with
+  // fewer than 16 row groups pack better at two per CU (paired, against three: C2, 3
+  // groups, +2.1% rounds/s; C3 B = 256, 9 groups, +1.0%), while C3 B = 512 (17 groups)
+  // keeps three (two: -1.6%); the boundary between 9 and 17 is set by these runs alone.
   const int64_t units_base = (int64_t)S * Hkv * p.row_groups;
-  const int64_t per_cu = D != 128 ? 2 : units_base * 4 <= cu_count() ? 1 : 3;
+  const int64_t per_cu = D != 128 ? 2 : units_base * 4 <= cu_count() ? 1 : p.row_groups < 16 ? 2 : 3;
   const int64_t target = per_cu * (int64_t)cu_count();
   const int64_t maxp = std::max<int64_t>(max_prefix, 0);
   const int64_t want = std::max<int64_t>(1, ceil_div(target, units_base));
